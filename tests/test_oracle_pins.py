@@ -1,0 +1,440 @@
+"""Pins of the float64 CPU oracle to facts other than itself.
+
+Each ``pin_*`` function checks the oracle against something it does not
+share code with: a library attention routine (torch's scaled-dot-product
+attention in float64) fed from an independently built paged pool, closed
+forms (one token, two tokens, zero query, saturated scores), exact
+invariances (physical block relabelling, prefix sharing, GQA vs repeated
+MHA, shift of all keys, linearity in V), the FP8 E4M3FN and bf16 format
+definitions against torch's own casts, and the KV sizes printed on the pages.
+``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle
+(on the CPU) and checks that every one of them breaks at least one pin.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import decode_attention as da
+from workloads import BLOCK_SIZE, Spec, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "kv_cache_sizes.txt")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+class AppendOnlyPool:
+    """A paged pool filled the way an engine appends decode tokens.
+
+    Each sequence owns a list of physical blocks.  A token is written at the
+    next free slot of the sequence's last block; when that block is full a
+    new one is taken from a shuffled free list ("LLM 推理优化" notes,
+    section 二).  Unwritten positions hold NaN so that any stray read shows.
+    """
+
+    def __init__(self, num_blocks, hkv, d, rng):
+        self.k = np.full((num_blocks, BLOCK_SIZE, hkv, d), np.nan)
+        self.v = np.full((num_blocks, BLOCK_SIZE, hkv, d), np.nan)
+        self.free = [int(x) for x in rng.permutation(num_blocks)]
+        self.blocks = {}
+        self.fill = {}
+
+    def append(self, seq, k, v):
+        blocks = self.blocks.setdefault(seq, [])
+        if not blocks or self.fill[seq] == BLOCK_SIZE:
+            blocks.append(self.free.pop())
+            self.fill[seq] = 0
+        blk, off = blocks[-1], self.fill[seq]
+        self.k[blk, off] = k
+        self.v[blk, off] = v
+        self.fill[seq] += 1
+
+    def table(self, nseq):
+        width = max([len(self.blocks.get(s, [])) for s in range(nseq)] + [1])
+        t = np.full((nseq, width), -1, np.int32)
+        for s in range(nseq):
+            row = self.blocks.get(s, [])
+            t[s, :len(row)] = row
+        return t
+
+
+def _sdpa(qb, K, V, scale):
+    """torch scaled-dot-product attention, float64, one sequence.
+
+    qb: [Hq, d]; K, V: [n, Hkv, d] contiguous in token order.
+    """
+    Hq, Hkv = qb.shape[0], K.shape[1]
+    qt = torch.from_numpy(qb)[None, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(K.transpose(1, 0, 2)))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(V.transpose(1, 0, 2)))[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, enable_gqa=Hq != Hkv)
+    return o[0, :, 0, :].numpy()
+
+
+def _oracle(q, k, v, table, ctx, scale, kv="f64", qd="f64", **kw):
+    return oracle.paged_decode_attention(q, k, v, table, np.asarray(ctx), scale,
+                                         kv_dtype=kv, q_dtype=qd, **kw)
+
+
+# ---------------------------------------------------------------------------
+# pins
+
+
+def _pin_library_attention(Hq, Hkv, d, lens, seed):
+    rng = _rng(seed)
+    B = len(lens)
+    Ks = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    Vs = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    q = rng.standard_normal((B, Hq, d))
+    nblk = sum((n + 15) // 16 for n in lens) + 3
+    pool = AppendOnlyPool(nblk, Hkv, d, rng)
+    for t in range(max(lens)):  # interleave the sequences' appends
+        for b, n in enumerate(lens):
+            if t < n:
+                pool.append(b, Ks[b][t], Vs[b][t])
+    scale = 1.0 / math.sqrt(d)
+    got = _oracle(q, pool.k, pool.v, pool.table(B), lens, scale)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0.0)
+        else:
+            np.testing.assert_allclose(got[b], _sdpa(q[b], Ks[b], Vs[b], scale),
+                                       rtol=0, atol=1e-12)
+
+
+def pin_library_attention_mha():
+    _pin_library_attention(4, 4, 16, [1, 15, 16, 17, 50, 0], seed=11)
+
+
+def pin_library_attention_gqa():
+    _pin_library_attention(8, 2, 32, [33, 5, 64, 100], seed=12)
+
+
+def pin_library_attention_mqa():
+    _pin_library_attention(6, 1, 8, [7, 48, 49], seed=13)
+
+
+def pin_minimal_step_by_step():
+    """The growing single-head cache of "KV Cache 深度解析" section 六.
+
+    At every step the token's k/v is appended, then its q attends over the
+    whole cache.  Re-stated here with a contiguous cache; the oracle, given
+    the same tokens in a paged pool, must give the same output each step.
+    """
+    rng = _rng(21)
+    d, steps = 8, 40
+    qs, ks, vs = (rng.standard_normal((steps, d)) for _ in range(3))
+    pool = AppendOnlyPool(8, 1, d, rng)
+    kc = np.zeros((0, d))
+    vc = np.zeros((0, d))
+    for i in range(steps):
+        kc = np.concatenate([kc, ks[i][None]])
+        vc = np.concatenate([vc, vs[i][None]])
+        e = np.exp(qs[i] @ kc.T / math.sqrt(d) - (qs[i] @ kc.T / math.sqrt(d)).max())
+        want = (e / e.sum()) @ vc
+        pool.append(0, ks[i][None], vs[i][None])
+        got = _oracle(qs[i][None, None], pool.k, pool.v, pool.table(1), [i + 1],
+                      1.0 / math.sqrt(d))
+        np.testing.assert_allclose(got[0, 0], want, rtol=0, atol=1e-13)
+
+
+def _single_seq_pool(K, V, rng, extra=2):
+    """Place tokens K, V ([n, Hkv, d]) of one sequence at random blocks."""
+    n, hkv, d = K.shape
+    pool = AppendOnlyPool((n + 15) // 16 + extra, hkv, d, rng)
+    for t in range(n):
+        pool.append(0, K[t], V[t])
+    return pool
+
+
+def pin_single_token_is_its_value():
+    rng = _rng(31)
+    K, V = rng.standard_normal((1, 2, 16)), rng.standard_normal((1, 2, 16))
+    q = 50.0 * rng.standard_normal((1, 4, 16))
+    pool = _single_seq_pool(K, V, rng)
+    got = _oracle(q, pool.k, pool.v, pool.table(1), [1], 0.25)
+    assert np.array_equal(got[0, :2], np.broadcast_to(V[0, 0], (2, 16)))
+    assert np.array_equal(got[0, 2:], np.broadcast_to(V[0, 1], (2, 16)))
+
+
+def pin_two_tokens_logistic():
+    rng = _rng(32)
+    d = 16
+    K, V = rng.standard_normal((2, 1, d)), rng.standard_normal((2, 1, d))
+    q = rng.standard_normal((1, 1, d))
+    scale = 0.3
+    pool = _single_seq_pool(K, V, rng)
+    got = _oracle(q, pool.k, pool.v, pool.table(1), [2], scale)[0, 0]
+    s0, s1 = scale * (q[0, 0] @ K[0, 0]), scale * (q[0, 0] @ K[1, 0])
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    np.testing.assert_allclose(got, w0 * V[0, 0] + (1 - w0) * V[1, 0], rtol=0, atol=1e-14)
+
+
+def pin_zero_query_is_mean():
+    rng = _rng(33)
+    n, d = 37, 8
+    K, V = rng.standard_normal((n, 1, d)), rng.standard_normal((n, 1, d))
+    pool = _single_seq_pool(K, V, rng)
+    got = _oracle(np.zeros((1, 2, d)), pool.k, pool.v, pool.table(1), [n], 0.5)[0]
+    for h in range(2):
+        np.testing.assert_allclose(got[h], V[:, 0].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def pin_saturated_scores_pick_the_max():
+    """Huge scores: the softmax becomes a one-hot on the largest score."""
+    rng = _rng(34)
+    n, d = 40, 8
+    K, V = rng.standard_normal((n, 1, d)), rng.standard_normal((n, 1, d))
+    q = rng.standard_normal((1, 1, d))
+    sc = K[:, 0] @ q[0, 0]
+    assert np.sort(sc)[-1] - np.sort(sc)[-2] > 1e-3
+    pool = _single_seq_pool(K, V, rng)
+    got = _oracle(q * 1e6, pool.k, pool.v, pool.table(1), [n], 1.0)[0, 0]
+    assert np.array_equal(got, V[int(np.argmax(sc)), 0])
+
+
+def pin_shift_of_all_keys_is_invisible():
+    rng = _rng(35)
+    n, hkv, d = 50, 2, 16
+    K, V = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    q = rng.standard_normal((1, 4, d))
+    u = rng.standard_normal((1, hkv, d))
+    a = _single_seq_pool(K, V, _rng(1))
+    b = _single_seq_pool(K + u, V, _rng(1))
+    ga = _oracle(q, a.k, a.v, a.table(1), [n], 0.25)
+    gb = _oracle(q, b.k, b.v, b.table(1), [n], 0.25)
+    np.testing.assert_allclose(gb, ga, rtol=0, atol=1e-12)
+
+
+def pin_linear_in_values():
+    rng = _rng(36)
+    n, hkv, d = 45, 2, 16
+    K, V1, V2 = (rng.standard_normal((n, hkv, d)) for _ in range(3))
+    q = rng.standard_normal((1, 4, d))
+    outs = []
+    for V in (V1, V2, V1 + 2.0 * V2):
+        p = _single_seq_pool(K, V, _rng(2))
+        outs.append(_oracle(q, p.k, p.v, p.table(1), [n], 0.25))
+    np.testing.assert_allclose(outs[2], outs[0] + 2.0 * outs[1], rtol=0, atol=1e-12)
+
+
+_SMALL = Spec(name="pin_small", batch=4, num_q_heads=8, num_kv_heads=2, head_dim=32,
+              kv_dtype="f32", q_dtype="f32", seed=41, context_lens=(1, 16, 33, 90),
+              pool_blocks=20)
+
+
+def pin_block_relabelling_is_bit_exact():
+    inp = make_inputs(_SMALL)
+    base = _oracle(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens,
+                   inp.scale, kv="f32", qd="f32")
+    pi = _rng(42).permutation(inp.num_blocks)
+    k2 = np.empty_like(inp.k_pool)
+    v2 = np.empty_like(inp.v_pool)
+    k2[pi] = inp.k_pool
+    v2[pi] = inp.v_pool
+    t2 = np.where(inp.block_table >= 0, pi[np.maximum(inp.block_table, 0)], -1)
+    got = _oracle(inp.q, k2, v2, t2, inp.context_lens, inp.scale, kv="f32", qd="f32")
+    assert np.array_equal(got, base)
+
+
+def pin_prefix_sharing_is_bit_exact():
+    spec = Spec(name="pin_prefix", batch=5, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                kv_dtype="bf16", q_dtype="bf16", seed=43, ctx_range=(40, 120),
+                shared_prefix_seqs=3, shared_prefix_tokens=32)
+    inp = make_inputs(spec)
+    shared = inp.block_table[:3, :2]
+    assert (shared == shared[0]).all()
+    base = _oracle(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens,
+                   inp.scale, kv="bf16", qd="bf16")
+    # give sequences 1 and 2 private copies of the prefix blocks
+    k, v, t = inp.k_pool, inp.v_pool, inp.block_table.copy()
+    for b in (1, 2):
+        new = np.arange(k.shape[0], k.shape[0] + 2)
+        k = np.concatenate([k, k[t[b, :2]]])
+        v = np.concatenate([v, v[t[b, :2]]])
+        t[b, :2] = new
+    got = _oracle(inp.q, k, v, t, inp.context_lens, inp.scale, kv="bf16", qd="bf16")
+    assert np.array_equal(got, base)
+
+
+def pin_gqa_is_repeated_mha():
+    inp = make_inputs(_SMALL)
+    G = _SMALL.num_q_heads // _SMALL.num_kv_heads
+    gqa = _oracle(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens,
+                  inp.scale, kv="f32", qd="f32")
+    k = np.repeat(inp.k_pool, G, axis=2)
+    v = np.repeat(inp.v_pool, G, axis=2)
+    mha = _oracle(inp.q, k, v, inp.block_table, inp.context_lens, inp.scale,
+                  kv="f32", qd="f32")
+    np.testing.assert_allclose(mha, gqa, rtol=0, atol=1e-15)
+
+
+_FP8 = Spec(name="pin_fp8", batch=3, num_q_heads=4, num_kv_heads=2, head_dim=32,
+            kv_dtype="fp8_e4m3", q_dtype="bf16", seed=44, context_lens=(5, 31, 70),
+            pool_blocks=12)
+
+
+def _dequant_with_torch(codes, sc):
+    """codes [N][16][Hkv][d], scales [N][Hkv][16] -> float64 [N][16][Hkv][d]."""
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return vals * sc.astype(np.float64).transpose(0, 2, 1)[..., None]
+
+
+def pin_fp8_equals_dequantised_values():
+    inp = make_inputs(_FP8)
+    got = _oracle(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens,
+                  inp.scale, kv="fp8_e4m3", qd="bf16", k_scale=inp.k_scale,
+                  v_scale=inp.v_scale)
+    kd = _dequant_with_torch(inp.k_pool, inp.k_scale)
+    vd = _dequant_with_torch(inp.v_pool, inp.v_scale)
+    want = _oracle(inp.q, kd, vd, inp.block_table, inp.context_lens, inp.scale,
+                   kv="f64", qd="bf16")
+    assert np.array_equal(got, want)
+
+
+def pin_fp8_close_to_unquantised():
+    """E4M3 keeps 3 mantissa bits: values move by at most 1/16 relative."""
+    spec = _FP8
+    q8 = make_inputs(spec)
+    f = make_inputs(Spec(**{**spec.__dict__, "kv_dtype": "f32"}))
+    a = _oracle(q8.q, q8.k_pool, q8.v_pool, q8.block_table, q8.context_lens, q8.scale,
+                kv="fp8_e4m3", qd="bf16", k_scale=q8.k_scale, v_scale=q8.v_scale)
+    b = _oracle(f.q, f.k_pool, f.v_pool, f.block_table, f.context_lens, f.scale,
+                kv="f32", qd="bf16")
+    assert np.abs(a - b).max() < 0.1
+
+
+def pin_e4m3fn_format():
+    vals = oracle.E4M3FN_TABLE
+    lib = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    lib = lib.to(torch.float64).numpy()
+    nan = np.isnan(vals)
+    assert np.array_equal(nan, np.isnan(lib))
+    assert np.array_equal(vals[~nan], lib[~nan])
+    assert set(np.flatnonzero(nan)) == {0x7F, 0xFF}
+    assert vals[0x7E] == 448.0 and np.nanmax(vals) == 448.0
+    assert vals[0x01] == 2.0 ** -9 and vals[0x08] == 2.0 ** -6
+    assert np.all(np.diff(vals[:0x7F]) > 0)
+    assert np.array_equal(vals[0x80:0xFF], -vals[:0x7F])
+
+
+def pin_bf16_format():
+    bits = np.arange(0, 1 << 16, 7, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_bits_to_f64(bits)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], lib[~nan])
+
+
+def _golden_rows():
+    rows = []
+    with open(GOLDEN, encoding="utf-8") as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, args, val, unit, tol, src = [c.strip() for c in line.split("|")]
+            rows.append((name, [float(x) for x in args.split()], float(val), unit,
+                         float(tol), src))
+    return rows
+
+
+_UNIT = {"KB": 2 ** 10, "MB": 2 ** 20, "GB": 2 ** 30}
+
+
+def pin_kv_sizes_printed_on_the_pages():
+    rows = _golden_rows()
+    assert len(rows) >= 9
+    for name, args, val, unit, tol, _src in rows:
+        got = oracle.kv_cache_bytes(*args)
+        want = val * _UNIT[unit]
+        assert abs(got - want) <= tol * want, (name, got, want)
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+def test_gqa_and_mha_sizes():
+    """GQA with 32 query / 8 KV heads stores a quarter of MHA's KV.
+
+    "KV Cache 深度解析" section 四 states the factor 4; its per-token MHA
+    figure of 8 KB disagrees with that factor and with the page's own
+    closed form (16 KiB for 32 KV heads x 128 x 2 B x 2), which is what
+    section 七's 16 GB -> 64 GB also implies.  The closed form governs.
+    """
+    mha = oracle.kv_cache_bytes(1, 32, 128, 1, 1, 2)
+    gqa = oracle.kv_cache_bytes(1, 8, 128, 1, 1, 2)
+    assert mha == 16384 and mha / gqa == 4
+
+
+def test_cpu_offload_time():
+    """"KV Cache 深度解析" section 七: 512 MB per token over ~32 GB/s is ~16 ms."""
+    per_step = oracle.kv_cache_bytes(32, 8, 128, 4096, 1, 2)
+    for link in (32 * 2 ** 30, 32e9):
+        assert abs(per_step / link - 0.016) / 0.016 < 0.06
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must break at least one pin
+
+
+def _gather_v_from_k(k_pool, v_pool, table_row, n, kv_head, kv_dtype, k_scale=None,
+                     v_scale=None):
+    K, _ = _REAL_GATHER(k_pool, v_pool, table_row, n, kv_head, kv_dtype, k_scale, v_scale)
+    return K, K
+
+
+def _gather_drops_newest(k_pool, v_pool, table_row, n, kv_head, kv_dtype, k_scale=None,
+                         v_scale=None):
+    K, V = _REAL_GATHER(k_pool, v_pool, table_row, max(n - 1, 1), kv_head, kv_dtype,
+                        k_scale, v_scale)
+    return K, V
+
+
+def _gather_v_unscaled(k_pool, v_pool, table_row, n, kv_head, kv_dtype, k_scale=None,
+                       v_scale=None):
+    K, V = _REAL_GATHER(k_pool, v_pool, table_row, n, kv_head, kv_dtype, k_scale, None
+                        if kv_dtype != "fp8_e4m3" else np.ones_like(v_scale))
+    return K, V
+
+
+_REAL_GATHER = da.gather_sequence_head
+
+MUTANTS = {
+    "slot_and_block_swapped": ("token_position", lambda t: (t % 16, t // 16)),
+    "blocks_of_8": ("token_position", lambda t: (t // 8, t % 8)),
+    "interleaved_groups": ("kv_head_of", lambda h, hq, hkv: h % hkv),
+    "unscaled_scores": ("scores", lambda K, q, scale: K @ q),
+    "sqrt_scale": ("scores", lambda K, q, scale: math.sqrt(scale) * (K @ q)),
+    "no_normalisation": ("softmax", lambda s: np.exp(s - s.max())),
+    "no_max_subtraction": ("softmax", lambda s: np.exp(s) / np.exp(s).sum()),
+    "values_read_from_keys": ("gather_sequence_head", _gather_v_from_k),
+    "newest_token_dropped": ("gather_sequence_head", _gather_drops_newest),
+    "fp8_value_scale_ignored": ("gather_sequence_head", _gather_v_unscaled),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistakes_are_caught(mutant, monkeypatch):
+    attr, fn = MUTANTS[mutant]
+    monkeypatch.setattr(da, attr, fn)
+    broken = []
+    with np.errstate(all="ignore"):
+        for pin in PINS:
+            try:
+                pin()
+            except Exception:  # an assertion or a crash: the pin noticed
+                broken.append(pin.__name__)
+    assert broken, f"no pin catches the planted mistake {mutant!r}"
