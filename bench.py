@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Decode-attention bandwidth benchmark on one MI355X.
+
+One step = one decode-attention call (partition kernel + merge kernel) for
+one layer of the Llama-3-8B-shaped workload: batch 32, 32 query / 8 KV heads,
+head_dim 128, every context 4096 tokens, bf16 KV in 16-token blocks placed by
+a seeded random permutation of an 8192-block pool.  Inputs are synthetic and
+resident in HBM before timing starts.  The timed loop cycles over
+``--layers`` independent copies of the KV pool (different layers' caches),
+so no step finds its 512 MiB of KV in the 256 MB Infinity Cache that the
+previous step filled.
+
+Printed: one JSON line on stdout.  ``value`` is KV bytes read per step
+(unique cached tokens x KV heads x head_dim x 2 (K and V) x element bytes)
+over the wall-clock time per step of the K timed steps.  ``roofline`` prices
+the partition kernel alone (HIP events around every launch in the timed
+loop) against MI355X's 8 TB/s HBM peak.  ``cpu_baseline`` times the float64
+CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-read TB/s, % of 8 TB/s HBM peak; µs per decode step"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_398_amd", "csrc", "pa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partition_kernel_llama3_8b_b32_ctx4k.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def kv_bytes(inp):
+    s = inp.spec
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[s.kv_dtype]
+    per_token = s.num_kv_heads * s.head_dim * 2 * eb
+    if s.kv_dtype == "fp8_e4m3":
+        per_token += s.num_kv_heads * 2 * 4
+    return inp.unique_tokens * per_token
+
+
+def stored_traffic():
+    """HBM bytes per launch from committed counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, seconds):
+    """The float64 oracle on whole sequences of the workload, ~``seconds``."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    s = inp.spec
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[s.kv_dtype]
+    done_tokens, n_seq = 0, 0
+    t0 = time.perf_counter()
+    b = 0
+    while True:
+        oracle.paged_decode_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                      inp.context_lens, inp.scale, kv_dtype=s.kv_dtype,
+                                      q_dtype=s.q_dtype, k_scale=inp.k_scale,
+                                      v_scale=inp.v_scale, seqs=[b])
+        done_tokens += int(inp.context_lens[b])
+        n_seq += 1
+        b = (b + 1) % s.batch
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = done_tokens * s.num_kv_heads * s.head_dim * 2 * eb
+    return {
+        "value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+        "host_cpus": os.cpu_count(),
+        "sample": f"{n_seq} whole sequences ({done_tokens} tokens x {s.num_kv_heads} KV heads) "
+                  f"of the same workload in {dt:.1f} s; float64 numpy, BLAS threads={threads}",
+        "seconds_per_step_equivalent": dt * inp.logical_tokens / max(done_tokens, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_b32_ctx4k")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="independent KV pools cycled by the timed loop")
+    ap.add_argument("--partition-tokens", type=int, default=0, help="0: automatic")
+    ap.add_argument("--cold-iters", type=int, default=30,
+                    help="extra steps timed after a 1 GiB cache flush each")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after the steps, run one plain device copy of this many MiB "
+                         "(reference for hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_398_amd as pa
+    from workloads import make_inputs, named_spec
+    from workloads.device import to_device
+
+    pa.load_library()  # raises if libpa.so is not built
+    log(f"generating {args.workload}")
+    inp = make_inputs(named_spec(args.workload))
+    s = inp.spec
+    dev = to_device(inp)
+    log("inputs resident on the GPU")
+    R = max(1, args.layers)
+    pools = []
+    for r in range(R):
+        k = dev.k_pool if r == 0 else dev.k_pool.clone()
+        v = dev.v_pool if r == 0 else dev.v_pool.clone()
+        ks = None if dev.k_scale is None else (dev.k_scale if r == 0 else dev.k_scale.clone())
+        vs = None if dev.v_scale is None else (dev.v_scale if r == 0 else dev.v_scale.clone())
+        p = pa.PagedKVPool(k, v, s.kv_dtype, ks, vs)
+        p.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
+        if args.partition_tokens:
+            p.set_partition_tokens(args.partition_tokens)
+        pools.append(p)
+    part_tokens = pools[0].partition_tokens()
+    ws_bytes = pools[0].workspace_bytes(s.num_q_heads)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    scale = float(inp.scale)
+
+    def step(i):
+        pools[i % R].decode(dev.q, out, ws if ws_bytes else None, scale=scale)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    per_pool = (args.steps + R - 1) // R
+    for p in pools:
+        pa.pa_profile_enable(p.handle, per_pool)
+    log(f"timing {args.steps} steps (partition {part_tokens} tokens, {R} layers)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    part_ms, merge_ms = [], []
+    for p in pools:
+        a, b = pa.pa_profile_read(p.handle, per_pool)
+        part_ms += a
+        merge_ms += b
+        pa.pa_profile_enable(p.handle, 0)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite output")
+
+    nbytes = kv_bytes(inp)
+    sec_per_step = (t1 - t0) / args.steps
+    tbs = nbytes / sec_per_step / 1e12
+    part_avg = statistics.fmean(part_ms) * 1e-3
+    merge_avg = statistics.fmean(merge_ms) * 1e-3
+    achieved = nbytes / part_avg / 1e9
+    log(f"{sec_per_step * 1e6:.1f} us/step, {tbs:.3f} TB/s; partition kernel "
+        f"{part_avg * 1e6:.1f} us ({achieved:.0f} GB/s), merge {merge_avg * 1e6:.1f} us")
+
+    # cold steps: every step after writing 1 GiB elsewhere (flush outside the events)
+    cold = []
+    if args.cold_iters > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(args.cold_iters):
+            flush.fill_(float(i))
+            ev0.record()
+            step(i)
+            ev1.record()
+            ev1.synchronize()
+            cold.append(ev0.elapsed_time(ev1) * 1e-3)
+        del flush
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibration_copy_mib} MiB read + written")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    traffic = stored_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": s.name, "batch": s.batch, "q_heads": s.num_q_heads,
+            "kv_heads": s.num_kv_heads, "head_dim": s.head_dim,
+            "context_tokens": int(inp.max_context_len), "block_size": 16,
+            "kv_dtype": s.kv_dtype, "q_dtype": s.q_dtype, "out_dtype": "f32",
+            "kv_bytes_per_step": nbytes, "partition_tokens": part_tokens,
+            "layers_cycled": R,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "partition_kernel", "kernel_us": round(part_avg * 1e6, 2),
+            "merge_us": round(merge_avg * 1e6, 2),
+        },
+        "us_per_step": round(sec_per_step * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2),
+        "cold": None if not cold else {
+            "median_step_us": round(statistics.median(cold) * 1e6, 2),
+            "tb_s": round(nbytes / statistics.median(cold) / 1e12, 4),
+            "iters": len(cold),
+            "note": "one step after writing 1 GiB elsewhere; event-timed step",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    for p in pools:
+        p.close()
+
+
+if __name__ == "__main__":
+    main()

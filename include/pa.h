@@ -1,0 +1,236 @@
+/*
+ * pa.h -- single-token decode attention over a paged KV cache (C ABI).
+ *
+ * Operation.  For every sequence b and query head h of one decode step:
+ *
+ *     out[b][h][:] = softmax_t( scale * q[b][h][:] . K_b[t][g][:] ) V_b[t][g][:]
+ *
+ * over the sequence's cached tokens t = 0 .. context_lens[b]-1, where
+ * g = h / (num_q_heads / num_kv_heads) is the KV head of h's group and token
+ * t lives in physical block block_table[b][t / 16] at slot t % 16.
+ *
+ * Sources (page title and section):
+ *   - attention softmax(Q K^T / sqrt(d)) V and the decode step that reuses
+ *     every cached K/V of the sequence, the new token's own included:
+ *     "KV Cache 深度解析:显存黑洞、PagedAttention 与三路省内存方案" (d7kj.com),
+ *     sections 一 and 六;
+ *   - fixed 16-token blocks and a per-sequence logical->physical block
+ *     table, with blocks free to be shared between sequences: same page,
+ *     section 三 (PagedAttention);
+ *   - in-block layout [block_size][heads][head_dim], K and V stored apart:
+ *     LLM inference-optimization notes (qingdujian.com), section 二;
+ *   - query heads in groups sharing one K/V head (GQA; MHA and MQA as the
+ *     two ends): "大模型推理为何这么慢？从内存带宽瓶颈到KV Cache优化的技术突围"
+ *     (answer.freetools.me), section on GQA and MQA;
+ *   - FP8 E4M3 KV with per-token, per-head scales: d7kj.com page, section 四.
+ *
+ * The pages leave open which query heads form a group; this library takes
+ * contiguous groups (h / G).
+ *
+ * Conventions shared by every call.
+ *   - Pointers named "device" point to GPU memory of the current HIP device;
+ *     the caller allocates, owns and frees all of them.  The library never
+ *     allocates or frees device memory; it owns only the host-side handle.
+ *   - Work is enqueued asynchronously on the caller's stream (a hipStream_t
+ *     passed as void*; NULL is the default stream).  No call synchronises,
+ *     except pa_block_table_validate.  Device buffers must stay valid until
+ *     the enqueued work completes.
+ *   - Every call validates its arguments on the host before any HIP call
+ *     and returns a pa_status.  On failure nothing is enqueued and
+ *     pa_last_error() (thread-local) holds a one-line description.
+ *   - Device-side data (block ids, context lengths) are not read by the
+ *     host unless pa_block_table_validate is called.  Invalid device data
+ *     give undefined *values* in out, never an out-of-bounds access: the
+ *     kernels clamp lengths to max_context_len and skip block ids outside
+ *     [0, num_blocks).
+ *   - A handle is not thread-safe; distinct handles are independent.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Tokens per physical block (fixed). */
+#define PA_BLOCK_SIZE 16
+
+typedef struct pa_kv_pool pa_kv_pool; /* opaque host-side handle */
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,      /* IEEE binary32                                  */
+  PA_DTYPE_BF16 = 1,     /* upper 16 bits of binary32                      */
+  PA_DTYPE_FP8_E4M3 = 2  /* OCP E4M3FN: bias 7, max 448, NaN = S.1111.111  */
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  PA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent        */
+  PA_ERR_DTYPE = 3,       /* dtype unknown, or wrong for this entry point  */
+  PA_ERR_UNSUPPORTED = 4, /* valid but not built: head_dim, group size     */
+  PA_ERR_STATE = 5,       /* e.g. run before a block table was set         */
+  PA_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned    */
+  PA_ERR_HIP = 7          /* the HIP runtime reported an error             */
+} pa_status;
+
+/*
+ * pa_kv_pool_create -- describe a physical block pool (no allocation).
+ *
+ * k_cache, v_cache: device, [num_blocks][16][num_kv_heads][head_dim] of
+ *   kv_dtype, each 16-byte aligned (the block pool of the d7kj.com page,
+ *   section 三; layout of the qingdujian.com notes, section 二).
+ * k_scale, v_scale: device, float32 [num_blocks][num_kv_heads][16] -- one
+ *   scale per (block, KV head, slot), i.e. per token and head (d7kj.com
+ *   page, section 四); the stored value is e4m3(code) * scale.  Required
+ *   when kv_dtype is PA_DTYPE_FP8_E4M3, must be NULL otherwise.
+ * block_size must be 16; head_dim must be 64 or 128; num_kv_heads >= 1;
+ * num_blocks >= 1.
+ * On success *out_pool receives a new handle (free with pa_kv_pool_destroy).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED.
+ */
+pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                            int32_t head_dim, pa_dtype kv_dtype, const void *k_cache,
+                            const void *v_cache, const float *k_scale, const float *v_scale,
+                            pa_kv_pool **out_pool);
+
+/* pa_kv_pool_destroy -- free the handle (NULL is ignored).  Device buffers
+ * are untouched.  Work already enqueued is unaffected. */
+void pa_kv_pool_destroy(pa_kv_pool *pool);
+
+/*
+ * pa_block_table_set -- point the handle at this step's block tables.
+ *
+ * block_table: device int32 [batch][max_blocks_per_seq]; entry j of row b
+ *   is the physical block holding tokens 16j .. 16j+15 of sequence b
+ *   (d7kj.com page, section 三).  Entries past a sequence's last block are
+ *   never read (pad them with -1).  Rows may share physical blocks (prefix
+ *   sharing).
+ * context_lens: device int32 [batch]; number of cached tokens each query
+ *   attends to, the new token's own K/V included (d7kj.com page, section 六).
+ *   0 is allowed and yields a zero output row.
+ * max_context_len: host upper bound of context_lens; it sizes the launch
+ *   grid and the workspace.  Must satisfy
+ *   0 <= max_context_len <= 16 * max_blocks_per_seq.  Lengths above it are
+ *   clamped to it by the kernels.
+ * Cheap (records pointers and sizes); call it every step.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (batch < 0, max_blocks_per_seq < 1,
+ *   max_context_len out of range).
+ */
+pa_status pa_block_table_set(pa_kv_pool *pool, const int32_t *block_table,
+                             const int32_t *context_lens, int32_t batch,
+                             int32_t max_blocks_per_seq, int32_t max_context_len);
+
+/*
+ * pa_block_table_validate -- debug check of the device tables (synchronous).
+ *
+ * Copies block_table and context_lens to the host on `stream`, waits, and
+ * checks 0 <= context_lens[b] <= max_context_len and that every entry a
+ * sequence uses lies in [0, num_blocks).
+ * Errors: PA_ERR_STATE (no table set), PA_ERR_SHAPE (a check failed; the
+ *   first offending sequence is named in pa_last_error), PA_ERR_HIP.
+ */
+pa_status pa_block_table_validate(pa_kv_pool *pool, void *stream);
+
+/*
+ * pa_decode_workspace_bytes -- device scratch a decode run needs.
+ *
+ * The context of each sequence is split into partitions processed in
+ * parallel; each writes a running max, a running sum and an unnormalised
+ * output per query head, later combined exactly by a log-sum-exp merge.
+ * The size depends on the table set last (batch, max_context_len), the
+ * partition length in force and num_q_heads.  *bytes receives the size
+ * (0 when nothing needs storing).
+ * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_SHAPE.
+ */
+pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads,
+                                    size_t *bytes);
+
+/*
+ * pa_decode_run -- one decode step over an f32 or bf16 pool.
+ *
+ * q: device [batch][num_q_heads][head_dim] of q_dtype (PA_DTYPE_F32 with an
+ *   f32 pool, PA_DTYPE_BF16 with a bf16 pool).
+ * num_q_heads: a multiple of num_kv_heads with group size
+ *   num_q_heads/num_kv_heads in {1, 2, 4, 8}.
+ * scale: softmax scale, normally 1/sqrt(head_dim) (d7kj.com page, section 一).
+ * out: device float32 [batch][num_q_heads][head_dim], written in full.
+ * workspace: device, 256-byte aligned, at least pa_decode_workspace_bytes;
+ *   its contents are scratch (no need to clear).  May be NULL when that
+ *   size is 0.
+ * stream: hipStream_t of the caller.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE (pool is FP8, or q_dtype
+ *   does not match), PA_ERR_UNSUPPORTED (group size), PA_ERR_STATE (no
+ *   table set), PA_ERR_WORKSPACE, PA_ERR_HIP (launch failed; out undefined).
+ */
+pa_status pa_decode_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                        int32_t num_q_heads, float scale, float *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_fp8_run -- one decode step over an FP8 E4M3 pool.
+ *
+ * Same arguments and outputs as pa_decode_run; the pool must have been
+ * created with PA_DTYPE_FP8_E4M3 and scales, and q_dtype must be
+ * PA_DTYPE_BF16.  Keys and values are dequantised in registers as
+ * e4m3(code) * scale (d7kj.com page, section 四); accumulation and output
+ * are float32.
+ * Errors: as pa_decode_run; PA_ERR_DTYPE if the pool is not FP8.
+ */
+pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                            int32_t num_q_heads, float scale, float *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_set_partition_tokens -- override the context partition length.
+ *
+ * tokens: 0 restores the automatic choice; otherwise a multiple of 16 in
+ * [16, 1 << 20].  Any value gives the same result up to rounding (the
+ * merge is exact); it only changes parallelism and workspace size.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
+ */
+pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens);
+
+/*
+ * pa_decode_partition_tokens -- partition length the next run will use for
+ * the table set last (after the automatic choice or an override).
+ * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set).
+ */
+pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens);
+
+/*
+ * pa_profile_enable -- time the attention kernel of the next runs.
+ *
+ * While enabled (capacity > 0), each run records a pair of HIP events on
+ * its stream around its partition kernel and another around its merge
+ * kernel, for up to `capacity` runs; capacity 0 disables and releases the
+ * events.  Events are host-side HIP objects, not device memory.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (capacity < 0), PA_ERR_HIP.
+ */
+pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity);
+
+/*
+ * pa_profile_read -- per-run kernel durations recorded since enabling.
+ *
+ * Waits for the recorded events, writes up to `capacity` durations in
+ * milliseconds to partition_ms[i] and merge_ms[i] (either may be NULL) and
+ * the number of recorded runs to *count, then starts a new recording.
+ * Errors: PA_ERR_NULL, PA_ERR_STATE (profiling not enabled), PA_ERR_HIP.
+ */
+pa_status pa_profile_read(pa_kv_pool *pool, float *partition_ms, float *merge_ms,
+                          int32_t capacity, int32_t *count);
+
+/* Static text for a status code. */
+const char *pa_status_str(pa_status status);
+
+/* Description of the last failure on this thread ("" if none). */
+const char *pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

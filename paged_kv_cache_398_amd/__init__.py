@@ -1,0 +1,87 @@
+"""Single-token decode attention over a paged KV cache on MI355X (gfx950).
+
+The computation lives in ``lib/libpa.so`` (C ABI in ``include/pa.h``; HIP
+kernels in ``csrc/``).  :mod:`.binding` exposes the C functions under their
+own names; :class:`PagedKVPool` is a small owner of one pool handle that
+keeps the tensors it was given alive.  PyTorch is used only for device
+memory and streams.
+"""
+
+from .binding import (  # noqa: F401
+    PA_BLOCK_SIZE,
+    PA_DTYPE,
+    PAError,
+    load_library,
+    pa_block_table_set,
+    pa_block_table_validate,
+    pa_decode_fp8_run,
+    pa_decode_partition_tokens,
+    pa_decode_run,
+    pa_decode_set_partition_tokens,
+    pa_decode_workspace_bytes,
+    pa_kv_pool_create,
+    pa_kv_pool_destroy,
+    pa_last_error,
+    pa_profile_enable,
+    pa_profile_read,
+    pa_status_str,
+)
+
+
+class PagedKVPool:
+    """One physical block pool and the block tables of the current step.
+
+    ``k_cache``/``v_cache``: device tensors ``[num_blocks][16][Hkv][d]`` of
+    ``kv_dtype`` ("f32", "bf16" or "fp8_e4m3" -- any torch dtype of that
+    width; only the bytes matter); ``k_scale``/``v_scale``: device float32
+    ``[num_blocks][Hkv][16]`` for FP8.
+    """
+
+    def __init__(self, k_cache, v_cache, kv_dtype, k_scale=None, v_scale=None):
+        n, bs, hkv, d = k_cache.shape
+        self.kv_dtype = kv_dtype
+        self.num_kv_heads, self.head_dim = hkv, d
+        self._keep = [k_cache, v_cache, k_scale, v_scale]
+        self.handle = pa_kv_pool_create(n, bs, hkv, d, kv_dtype, k_cache, v_cache,
+                                        k_scale, v_scale)
+
+    def set_block_table(self, block_table, context_lens, max_context_len):
+        """``block_table``: device int32 [B][max_blocks]; ``context_lens``:
+        device int32 [B]; ``max_context_len``: host bound of the lengths."""
+        b, mb = block_table.shape
+        self._tables = [block_table, context_lens]
+        self.batch = b
+        pa_block_table_set(self.handle, block_table, context_lens, b, mb, max_context_len)
+
+    def set_partition_tokens(self, tokens):
+        pa_decode_set_partition_tokens(self.handle, tokens)
+
+    def partition_tokens(self):
+        return pa_decode_partition_tokens(self.handle)
+
+    def workspace_bytes(self, num_q_heads):
+        return pa_decode_workspace_bytes(self.handle, num_q_heads)
+
+    def decode(self, q, out, workspace, scale=None, stream=None):
+        """One decode step: ``q`` [B][Hq][d] (f32 for an f32 pool, else bf16)
+        -> ``out`` float32 [B][Hq][d].  ``workspace``: device tensor of at
+        least :meth:`workspace_bytes` bytes (256-byte aligned) or None when
+        that size is 0.  ``scale`` defaults to 1/sqrt(head_dim)."""
+        hq = q.shape[1]
+        qd = "f32" if self.kv_dtype == "f32" else "bf16"
+        if scale is None:
+            scale = 1.0 / self.head_dim ** 0.5
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        fn = pa_decode_fp8_run if self.kv_dtype == "fp8_e4m3" else pa_decode_run
+        fn(self.handle, q, qd, hq, scale, out, workspace, ws_bytes, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            pa_kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,177 @@
+"""ctypes binding of libpa.so (include/pa.h), argument marshalling only.
+
+Functions carry the C names.  Device buffers may be given as torch tensors
+(their ``data_ptr()`` is passed) or as integer addresses; streams as a
+``torch.cuda.Stream``, an integer ``hipStream_t`` or None (torch's current
+stream).  Every non-OK status raises :class:`PAError`.  There is no fallback:
+if the library is not built, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
+
+PA_BLOCK_SIZE = 16
+PA_DTYPE = {"f32": 0, "bf16": 1, "fp8_e4m3": 2}
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE = 0, 1, 2, 3
+PA_ERR_UNSUPPORTED, PA_ERR_STATE, PA_ERR_WORKSPACE, PA_ERR_HIP = 4, 5, 6, 7
+
+# (name, restype, argtypes) for every exported symbol of include/pa.h
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = [
+    ("pa_kv_pool_create", _i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                 ctypes.POINTER(_vp)]),
+    ("pa_kv_pool_destroy", None, [_vp]),
+    ("pa_block_table_set", _i32, [_vp, _vp, _vp, _i32, _i32, _i32]),
+    ("pa_block_table_validate", _i32, [_vp, _vp]),
+    ("pa_decode_workspace_bytes", _i32, [_vp, _i32, ctypes.POINTER(_sz)]),
+    ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
+    ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
+    ("pa_decode_set_partition_tokens", _i32, [_vp, _i32]),
+    ("pa_decode_partition_tokens", _i32, [_vp, ctypes.POINTER(_i32)]),
+    ("pa_profile_enable", _i32, [_vp, _i32]),
+    ("pa_profile_read", _i32, [_vp, ctypes.POINTER(_f32), ctypes.POINTER(_f32), _i32,
+                               ctypes.POINTER(_i32)]),
+    ("pa_status_str", ctypes.c_char_p, [_i32]),
+    ("pa_last_error", ctypes.c_char_p, []),
+]
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_name(status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _name(status: int) -> str:
+    return {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
+            4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_STATE", 6: "PA_ERR_WORKSPACE",
+            7: "PA_ERR_HIP"}.get(status, f"status {status}")
+
+
+_LIB = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libpa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with "
+                           "`python -m paged_kv_cache_398_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PAError(status, load_library().pa_last_error().decode())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _dtype(d) -> int:
+    return PA_DTYPE[d] if isinstance(d, str) else int(d)
+
+
+def pa_kv_pool_create(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype, k_cache,
+                      v_cache, k_scale=None, v_scale=None) -> int:
+    out = _vp()
+    _check(load_library().pa_kv_pool_create(num_blocks, block_size, num_kv_heads, head_dim,
+                                            _dtype(kv_dtype), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(k_scale), _ptr(v_scale), ctypes.byref(out)))
+    return out.value
+
+
+def pa_kv_pool_destroy(pool: int) -> None:
+    load_library().pa_kv_pool_destroy(pool)
+
+
+def pa_block_table_set(pool, block_table, context_lens, batch, max_blocks_per_seq,
+                       max_context_len) -> None:
+    _check(load_library().pa_block_table_set(pool, _ptr(block_table), _ptr(context_lens),
+                                             batch, max_blocks_per_seq, max_context_len))
+
+
+def pa_block_table_validate(pool, stream=None) -> None:
+    _check(load_library().pa_block_table_validate(pool, _stream(stream)))
+
+
+def pa_decode_workspace_bytes(pool, num_q_heads) -> int:
+    n = _sz()
+    _check(load_library().pa_decode_workspace_bytes(pool, num_q_heads, ctypes.byref(n)))
+    return n.value
+
+
+def pa_decode_run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes,
+                  stream=None) -> None:
+    _check(load_library().pa_decode_run(pool, _ptr(q), _dtype(q_dtype), num_q_heads,
+                                        float(scale), _ptr(out), _ptr(workspace),
+                                        workspace_bytes, _stream(stream)))
+
+
+def pa_decode_fp8_run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes,
+                      stream=None) -> None:
+    _check(load_library().pa_decode_fp8_run(pool, _ptr(q), _dtype(q_dtype), num_q_heads,
+                                            float(scale), _ptr(out), _ptr(workspace),
+                                            workspace_bytes, _stream(stream)))
+
+
+def pa_decode_set_partition_tokens(pool, tokens) -> None:
+    _check(load_library().pa_decode_set_partition_tokens(pool, tokens))
+
+
+def pa_decode_partition_tokens(pool) -> int:
+    t = _i32()
+    _check(load_library().pa_decode_partition_tokens(pool, ctypes.byref(t)))
+    return t.value
+
+
+def pa_profile_enable(pool, capacity) -> None:
+    _check(load_library().pa_profile_enable(pool, capacity))
+
+
+def pa_profile_read(pool, capacity) -> Tuple[list, list]:
+    part = (_f32 * max(capacity, 1))()
+    merge = (_f32 * max(capacity, 1))()
+    n = _i32()
+    _check(load_library().pa_profile_read(pool, part, merge, capacity, ctypes.byref(n)))
+    k = min(n.value, capacity)
+    return list(part[:k]), list(merge[:k])
+
+
+def pa_status_str(status) -> str:
+    return load_library().pa_status_str(status).decode()
+
+
+def pa_last_error() -> str:
+    return load_library().pa_last_error().decode()

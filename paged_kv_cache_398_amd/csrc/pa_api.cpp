@@ -1,0 +1,381 @@
+// pa_api.cpp -- the C ABI of include/pa.h: argument validation, partition
+// choice, workspace layout and kernel launches on the caller's stream.
+//
+// Every entry point validates on the host before touching the HIP runtime,
+// so argument errors are reported without a GPU.  The library allocates no
+// device memory; callers pass every buffer.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+struct pa_kv_pool {
+  int32_t num_blocks = 0, num_kv_heads = 0, head_dim = 0;
+  pa_dtype kv_dtype = PA_DTYPE_F32;
+  const void *k_cache = nullptr, *v_cache = nullptr;
+  const float *k_scale = nullptr, *v_scale = nullptr;
+  // block tables of the current step
+  bool table_set = false;
+  const int32_t *block_table = nullptr, *context_lens = nullptr;
+  int32_t batch = 0, max_blocks_per_seq = 0, max_context_len = 0;
+  int32_t partition_override = 0;  // 0: automatic
+  // profiling
+  int32_t prof_capacity = 0, prof_count = 0;
+  std::vector<hipEvent_t> prof_events;  // 3 per run: before, between, after
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pa_status ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+bool aligned(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int kind_of(pa_dtype t) {
+  switch (t) {
+    case PA_DTYPE_F32: return pa::KV_F32;
+    case PA_DTYPE_BF16: return pa::KV_BF16;
+    default: return pa::KV_FP8;
+  }
+}
+
+// MI355X: 256 compute units in 8 XCDs.  The partition choice (and so the
+// workspace size) depends only on the arguments, never on a runtime query.
+constexpr int kComputeUnits = 256;
+constexpr int kTargetWorkgroupsPerCU = 4;
+
+// Tokens per context partition.  Each workgroup (kWaves waves) takes one
+// partition of one (sequence, KV head); waves take whole 16-token blocks.
+// Prefer long partitions (fewer partial results to merge) as long as the
+// grid still offers kTargetWorkgroupsPerCU workgroups per compute unit.
+int32_t auto_partition_tokens(const pa_kv_pool *p) {
+  const int64_t units = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t target = (int64_t)kTargetWorkgroupsPerCU * kComputeUnits;
+  const int64_t ctx = p->max_context_len;
+  for (int bpw = 64; bpw >= 1; bpw /= 2) {  // blocks per wave
+    const int64_t tokens = (int64_t)bpw * PA_BLOCK_SIZE * pa::kWaves;
+    if (units * ((ctx + tokens - 1) / tokens) >= target) return (int32_t)tokens;
+  }
+  return PA_BLOCK_SIZE * pa::kWaves;
+}
+
+int32_t partition_tokens(const pa_kv_pool *p) {
+  return p->partition_override > 0 ? p->partition_override : auto_partition_tokens(p);
+}
+
+struct Layout {
+  int32_t part_tokens, parts;
+  size_t ml_bytes, acc_offset, total;
+};
+
+Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
+  Layout L{};
+  L.part_tokens = partition_tokens(p);
+  L.parts = (int32_t)((p->max_context_len + (int64_t)L.part_tokens - 1) / L.part_tokens);
+  const size_t recs = (size_t)p->batch * hq * L.parts;
+  L.ml_bytes = recs * sizeof(float2);
+  L.acc_offset = (L.ml_bytes + 255) & ~(size_t)255;
+  L.total = recs ? L.acc_offset + recs * p->head_dim * sizeof(float) : 0;
+  return L;
+}
+
+pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, float scale,
+              float *out, void *workspace, size_t ws_bytes, void *stream, bool fp8_entry) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  const bool fp8_pool = pool->kv_dtype == PA_DTYPE_FP8_E4M3;
+  if (fp8_entry && !fp8_pool)
+    return fail(PA_ERR_DTYPE, "pa_decode_fp8_run needs an FP8 E4M3 pool");
+  if (!fp8_entry && fp8_pool)
+    return fail(PA_ERR_DTYPE, "an FP8 pool must be run with pa_decode_fp8_run");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set (pa_block_table_set)");
+  const pa_dtype want_q = pool->kv_dtype == PA_DTYPE_F32 ? PA_DTYPE_F32 : PA_DTYPE_BF16;
+  if (q_dtype != want_q)
+    return fail(PA_ERR_DTYPE, "q dtype %d does not match the pool (needs %d)", (int)q_dtype,
+                (int)want_q);
+  if (hq < 1 || hq % pool->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                hq, pool->num_kv_heads);
+  const int group = hq / pool->num_kv_heads;
+  if (!pa::kernel_supported(kind_of(pool->kv_dtype), pool->head_dim, group))
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", group);
+  if (!(std::isfinite(scale)))
+    return fail(PA_ERR_SHAPE, "scale must be finite");
+  if (pool->batch > 0 && (!q || !out)) return fail(PA_ERR_NULL, "q or out is NULL");
+  const Layout L = workspace_layout(pool, hq);
+  if (L.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+    if (ws_bytes < L.total)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  }
+  const size_t wgs = (size_t)pool->batch * pool->num_kv_heads * L.parts;
+  if (wgs * pa::kWaves * 64 >= (size_t(1) << 32) || (size_t)pool->batch * hq >= (size_t(1) << 31))
+    return fail(PA_ERR_SHAPE, "launch grid too large (raise the partition length)");
+  if (pool->batch == 0) return ok();
+
+  // ---- from here on HIP is used
+  pa::LaunchArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.q = q;
+  a.table = pool->block_table;
+  a.ctx = pool->context_lens;
+  a.out = out;
+  a.ws_ml = static_cast<float2 *>(workspace);
+  a.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.acc_offset);
+  a.num_blocks = pool->num_blocks;
+  a.hkv = pool->num_kv_heads;
+  a.hq = hq;
+  a.d = pool->head_dim;
+  a.batch = pool->batch;
+  a.max_blocks = pool->max_blocks_per_seq;
+  a.max_ctx = pool->max_context_len;
+  a.part_tokens = L.part_tokens;
+  a.parts = L.parts;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.kv = kind_of(pool->kv_dtype);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool prof = pool->prof_capacity > 0 && pool->prof_count < pool->prof_capacity;
+  hipEvent_t *ev = prof ? &pool->prof_events[3 * (size_t)pool->prof_count] : nullptr;
+  hipError_t e = hipSuccess;
+  if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = pa::launch_partition(a, s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "partition kernel launch: %s", hipGetErrorString(e));
+  if (prof && (e = hipEventRecord(ev[1], s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = pa::launch_merge(a, s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  if (prof) {
+    if ((e = hipEventRecord(ev[2], s)) != hipSuccess)
+      return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    ++pool->prof_count;
+  }
+  return ok();
+}
+
+void release_events(pa_kv_pool *p) {
+  for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+  p->prof_events.clear();
+  p->prof_capacity = 0;
+  p->prof_count = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                            int32_t head_dim, pa_dtype kv_dtype, const void *k_cache,
+                            const void *v_cache, const float *k_scale, const float *v_scale,
+                            pa_kv_pool **out_pool) {
+  if (!out_pool) return fail(PA_ERR_NULL, "out_pool is NULL");
+  *out_pool = nullptr;
+  if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "k_cache or v_cache is NULL");
+  if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16 && kv_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "unknown kv dtype %d", (int)kv_dtype);
+  const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale))
+    return fail(PA_ERR_NULL, "an FP8 pool needs k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale))
+    return fail(PA_ERR_DTYPE, "scales are only meaningful for an FP8 pool");
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_SHAPE, "block_size %d: only %d is supported", block_size, PA_BLOCK_SIZE);
+  if (num_blocks < 1 || num_kv_heads < 1 || head_dim < 1)
+    return fail(PA_ERR_SHAPE, "num_blocks, num_kv_heads and head_dim must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if ((int64_t)num_kv_heads * head_dim * 4 * PA_BLOCK_SIZE > (int64_t)1 << 30)
+    return fail(PA_ERR_SHAPE, "num_kv_heads too large");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_SHAPE, "k_cache and v_cache must be 16-byte aligned");
+  if (fp8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return fail(PA_ERR_SHAPE, "scales must be 4-byte aligned");
+  pa_kv_pool *p = new (std::nothrow) pa_kv_pool();
+  if (!p) return fail(PA_ERR_SHAPE, "out of host memory");
+  p->num_blocks = num_blocks;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  p->kv_dtype = kv_dtype;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  p->k_scale = k_scale;
+  p->v_scale = v_scale;
+  *out_pool = p;
+  return ok();
+}
+
+void pa_kv_pool_destroy(pa_kv_pool *pool) {
+  if (!pool) return;
+  release_events(pool);
+  delete pool;
+}
+
+pa_status pa_block_table_set(pa_kv_pool *pool, const int32_t *block_table,
+                             const int32_t *context_lens, int32_t batch,
+                             int32_t max_blocks_per_seq, int32_t max_context_len) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (batch < 0) return fail(PA_ERR_SHAPE, "batch %d < 0", batch);
+  if (batch > 0 && (!block_table || !context_lens))
+    return fail(PA_ERR_NULL, "block_table or context_lens is NULL");
+  if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq must be >= 1");
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
+    return fail(PA_ERR_SHAPE, "max_context_len %d outside [0, 16 * max_blocks_per_seq = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * PA_BLOCK_SIZE);
+  if ((int64_t)batch * max_blocks_per_seq >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "block table too large");
+  pool->block_table = block_table;
+  pool->context_lens = context_lens;
+  pool->batch = batch;
+  pool->max_blocks_per_seq = max_blocks_per_seq;
+  pool->max_context_len = max_context_len;
+  pool->table_set = true;
+  return ok();
+}
+
+pa_status pa_block_table_validate(pa_kv_pool *pool, void *stream) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set");
+  if (pool->batch == 0) return ok();
+  const size_t nt = (size_t)pool->batch * pool->max_blocks_per_seq;
+  std::vector<int32_t> table(nt), ctx(pool->batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = hipMemcpyAsync(table.data(), pool->block_table, nt * 4, hipMemcpyDeviceToHost, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(ctx.data(), pool->context_lens, ctx.size() * 4, hipMemcpyDeviceToHost, s)) != hipSuccess ||
+      (e = hipStreamSynchronize(s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "reading the tables: %s", hipGetErrorString(e));
+  for (int32_t b = 0; b < pool->batch; ++b) {
+    const int32_t n = ctx[b];
+    if (n < 0 || n > pool->max_context_len)
+      return fail(PA_ERR_SHAPE, "context_lens[%d] = %d outside [0, %d]", b, n, pool->max_context_len);
+    const int32_t nb = (n + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t id = table[(size_t)b * pool->max_blocks_per_seq + j];
+      if (id < 0 || id >= pool->num_blocks)
+        return fail(PA_ERR_SHAPE, "block_table[%d][%d] = %d outside [0, %d)", b, j, id,
+                    pool->num_blocks);
+    }
+  }
+  return ok();
+}
+
+pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads, size_t *bytes) {
+  if (!pool || !bytes) return fail(PA_ERR_NULL, "pool or bytes is NULL");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set");
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  *bytes = workspace_layout(pool, num_q_heads).total;
+  return ok();
+}
+
+pa_status pa_decode_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t num_q_heads,
+                        float scale, float *out, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  return run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes, stream, false);
+}
+
+pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                            int32_t num_q_heads, float scale, float *out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes, stream, true);
+}
+
+pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (tokens != 0 && (tokens < PA_BLOCK_SIZE || tokens % PA_BLOCK_SIZE || tokens > (1 << 20)))
+    return fail(PA_ERR_SHAPE, "partition length %d: 0 or a multiple of 16 in [16, 2^20]", tokens);
+  pool->partition_override = tokens;
+  return ok();
+}
+
+pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens) {
+  if (!pool || !tokens) return fail(PA_ERR_NULL, "pool or tokens is NULL");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set");
+  *tokens = partition_tokens(pool);
+  return ok();
+}
+
+pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (capacity < 0) return fail(PA_ERR_SHAPE, "capacity %d < 0", capacity);
+  release_events(pool);
+  if (capacity == 0) return ok();
+  pool->prof_events.resize(3 * (size_t)capacity);
+  for (auto &e : pool->prof_events) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      release_events(pool);
+      return fail(PA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(r));
+    }
+  }
+  pool->prof_capacity = capacity;
+  return ok();
+}
+
+pa_status pa_profile_read(pa_kv_pool *pool, float *partition_ms, float *merge_ms,
+                          int32_t capacity, int32_t *count) {
+  if (!pool || !count) return fail(PA_ERR_NULL, "pool or count is NULL");
+  if (pool->prof_capacity == 0) return fail(PA_ERR_STATE, "profiling not enabled");
+  const int32_t n = pool->prof_count;
+  *count = n;
+  if (n > 0) {
+    hipError_t e = hipEventSynchronize(pool->prof_events[3 * (size_t)n - 1]);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+  }
+  for (int32_t i = 0; i < n && i < capacity; ++i) {
+    hipEvent_t *ev = &pool->prof_events[3 * (size_t)i];
+    float t0 = 0.f, t1 = 0.f;
+    hipError_t e = hipEventElapsedTime(&t0, ev[0], ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t1, ev[1], ev[2]);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    if (partition_ms) partition_ms[i] = t0;
+    if (merge_ms) merge_ms[i] = t1;
+  }
+  pool->prof_count = 0;
+  return ok();
+}
+
+const char *pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_SHAPE: return "bad shape or size";
+    case PA_ERR_DTYPE: return "bad dtype";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_STATE: return "bad state";
+    case PA_ERR_WORKSPACE: return "bad workspace";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

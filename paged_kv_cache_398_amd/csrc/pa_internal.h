@@ -1,0 +1,44 @@
+// Internal interface between the C-ABI layer (pa_api.cpp) and the kernels
+// (pa_kernels.hip).  Not installed; the public interface is include/pa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+// Waves per workgroup of the partition kernel.  The blocks of one partition
+// are dealt round-robin to the waves.
+constexpr int kWaves = 4;
+
+// Everything one decode launch needs; plain pointers into device memory.
+struct LaunchArgs {
+  const void *k_cache;      // [num_blocks][16][hkv][d]
+  const void *v_cache;
+  const float *k_scale;     // [num_blocks][hkv][16] (FP8 only)
+  const float *v_scale;
+  const void *q;            // [batch][hq][d]
+  const int32_t *table;     // [batch][max_blocks]
+  const int32_t *ctx;       // [batch]
+  float *out;               // [batch][hq][d]
+  float2 *ws_ml;            // [batch][hq][parts] (running max, running sum)
+  float *ws_acc;            // [batch][hq][parts][d] unnormalised output
+  int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx;
+  int32_t part_tokens;      // tokens per partition (multiple of 16)
+  int32_t parts;            // ceil(max_ctx / part_tokens)
+  float scale_log2e;        // softmax scale * log2(e)
+  int kv;                   // KvKind
+};
+
+// True when a kernel is built for (kv, head_dim, group size).
+bool kernel_supported(int kv, int d, int group);
+
+// Enqueue the partition kernel (grid batch*hkv*parts workgroups).
+hipError_t launch_partition(const LaunchArgs &a, hipStream_t stream);
+
+// Enqueue the log-sum-exp merge kernel (grid batch*hq workgroups).
+hipError_t launch_merge(const LaunchArgs &a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances are those of the decode-attention target: max abs error 2e-3 for
+f32/bf16 KV with fp32 accumulation, 3e-2 for FP8 KV against an oracle that
+dequantises the same codes with the same scales.
+"""
+
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_398_amd as pa
+from workloads import NAMED_SPECS, Inputs, Spec, make_inputs
+from workloads.device import to_device
+
+from gpu_util import TOL, gpu_decode, max_err, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=2)
+def named(name, poison=False):
+    return make_inputs(NAMED_SPECS[name], poison=poison)
+
+
+def _sample_seqs(inp, k=6):
+    ctx = inp.context_lens
+    B = len(ctx)
+    cand = [0, B - 1, int(np.argmax(ctx)), int(np.argmin(ctx)), B // 2]
+    if inp.spec.shared_prefix_seqs:
+        cand += [inp.spec.shared_prefix_seqs - 1, inp.spec.shared_prefix_seqs]
+    return sorted(set(c for c in cand if 0 <= c < B))[:k + 2]
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads, full size, automatic launch configuration
+
+
+@pytest.mark.parametrize("name", list(NAMED_SPECS))
+def test_named_workload(name):
+    say(f"[parity] {name}: generating")
+    inp = named(name)
+    say(f"[parity] {name}: gpu run, max_ctx={inp.max_context_len}")
+    got = gpu_decode(inp)
+    assert np.isfinite(got).all()
+    seqs = None if inp.logical_tokens <= 32 * 4096 else _sample_seqs(inp)
+    want = oracle_decode(inp, seqs)
+    err = max_err(got, want, seqs)
+    say(f"[parity] {name}: max abs err {err:.3e} over "
+        f"{'all' if seqs is None else seqs} sequences")
+    assert err <= TOL[inp.spec.kv_dtype]
+
+
+# ---------------------------------------------------------------------------
+# small shapes: several blocks and partitions, ragged tails, every build
+
+
+CTX_MIX = (1, 15, 16, 17, 100, 333, 0, 64, 65)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (8, 2), (16, 2)])
+def test_small_shapes(kv, d, hq, hkv):
+    spec = Spec(name="small", batch=len(CTX_MIX), num_q_heads=hq, num_kv_heads=hkv,
+                head_dim=d, kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16",
+                seed=1000 + d + hq + 7 * hkv, context_lens=CTX_MIX, pool_blocks=60)
+    inp = make_inputs(spec, poison=True)
+    want = oracle_decode(inp)
+    for part in (0, 16, 48, 128):
+        say(f"[parity] small kv={kv} d={d} hq={hq} hkv={hkv} part={part}")
+        got = gpu_decode(inp, part_tokens=part)
+        err = max_err(got, want)
+        assert err <= TOL[kv], (part, err)
+        assert np.all(got[CTX_MIX.index(0)] == 0.0)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_context_edges(kv):
+    P = 64
+    ctx = (0, 1, 15, 16, 17, 31, 33, P - 1, P, P + 1, 2 * P + 3, 1000)
+    spec = Spec(name="edges", batch=len(ctx), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                kv_dtype=kv, q_dtype="bf16", seed=77, context_lens=ctx)
+    inp = make_inputs(spec, poison=True)
+    want = oracle_decode(inp)
+    say(f"[parity] edges kv={kv}")
+    got = gpu_decode(inp, part_tokens=P)
+    assert max_err(got, want) <= TOL[kv]
+
+
+def test_all_empty_batch():
+    spec = Spec(name="empty", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                kv_dtype="bf16", q_dtype="bf16", seed=5, context_lens=(0, 0, 0))
+    inp = make_inputs(spec)
+    say("[parity] all-empty batch")
+    got = gpu_decode(inp)
+    assert np.all(got == 0.0)
+
+
+def test_partition_sweep():
+    spec = Spec(name="sweep", batch=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                kv_dtype="bf16", q_dtype="bf16", seed=88, context_lens=(4096, 4001, 77))
+    inp = make_inputs(spec)
+    want = oracle_decode(inp)
+    for part in (16, 64, 256, 512, 1024, 4096, 8192):
+        say(f"[parity] sweep part={part}")
+        got = gpu_decode(inp, part_tokens=part)
+        assert max_err(got, want) <= TOL["bf16"], part
+
+
+def test_long_single_partition():
+    """One partition per sequence: every wave loops over many blocks."""
+    spec = Spec(name="longpart", batch=2, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                kv_dtype="bf16", q_dtype="bf16", seed=89, context_lens=(20000, 9999))
+    inp = make_inputs(spec)
+    want = oracle_decode(inp)
+    say("[parity] one partition of 20000 tokens")
+    got = gpu_decode(inp, part_tokens=20000 // 16 * 16 + 16)
+    assert max_err(got, want) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# invariances of the GPU result itself
+
+
+def _relabel(inp, seed):
+    pi = np.random.default_rng(seed).permutation(inp.num_blocks)
+    k, v = np.empty_like(inp.k_pool), np.empty_like(inp.v_pool)
+    k[pi], v[pi] = inp.k_pool, inp.v_pool
+    ks = vs = None
+    if inp.k_scale is not None:
+        ks, vs = np.empty_like(inp.k_scale), np.empty_like(inp.v_scale)
+        ks[pi], vs[pi] = inp.k_scale, inp.v_scale
+    t = np.where(inp.block_table >= 0, pi[np.maximum(inp.block_table, 0)], -1).astype(np.int32)
+    out = Inputs(
+        spec=inp.spec, q=inp.q, k_pool=k, v_pool=v, k_scale=ks, v_scale=vs, block_table=t,
+        context_lens=inp.context_lens, scale=inp.scale, used_blocks=inp.used_blocks[np.argsort(pi)])
+    return out
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_gpu_block_relabelling_is_bit_exact(kv):
+    spec = Spec(name="relabel", batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                kv_dtype=kv, q_dtype="bf16", seed=91, context_lens=(700, 33, 1, 512))
+    inp = make_inputs(spec)
+    say(f"[parity] relabel kv={kv}")
+    a = gpu_decode(inp)
+    b = gpu_decode(_relabel(inp, 3))
+    assert np.array_equal(a, b)
+
+
+def test_gpu_prefix_sharing_is_bit_exact():
+    spec = Spec(name="prefix", batch=6, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                kv_dtype="bf16", q_dtype="bf16", seed=92, ctx_range=(300, 900),
+                shared_prefix_seqs=4, shared_prefix_tokens=256)
+    inp = make_inputs(spec)
+    say("[parity] prefix sharing")
+    a = gpu_decode(inp)
+    # private copies of the 16 prefix blocks for sequences 1..3
+    k, v, t = inp.k_pool, inp.v_pool, inp.block_table.copy()
+    for b in (1, 2, 3):
+        new = np.arange(k.shape[0], k.shape[0] + 16)
+        k = np.concatenate([k, k[t[b, :16]]])
+        v = np.concatenate([v, v[t[b, :16]]])
+        t[b, :16] = new
+    inp2 = Inputs(
+        spec=inp.spec, q=inp.q, k_pool=k, v_pool=v, k_scale=None, v_scale=None, block_table=t,
+        context_lens=inp.context_lens, scale=inp.scale, used_blocks=None)
+    b2 = gpu_decode(inp2)
+    assert np.array_equal(a, b2)
+    assert max_err(a, oracle_decode(inp)) <= TOL["bf16"]
+
+
+def test_deterministic():
+    inp = named("tiny_f32")
+    say("[parity] determinism")
+    a = gpu_decode(inp)
+    b = gpu_decode(inp)
+    assert np.array_equal(a, b)
+
+
+def test_poisoned_tiny_equals_clean():
+    say("[parity] poison tiny")
+    clean = gpu_decode(named("tiny_f32"))
+    dirty = gpu_decode(make_inputs(NAMED_SPECS["tiny_f32"], poison=True))
+    assert np.array_equal(clean, dirty)
+
+
+# ---------------------------------------------------------------------------
+# buffers the library must not touch outside their bounds
+
+
+def test_canaries_around_out_and_workspace():
+    inp = make_inputs(Spec(name="canary", batch=3, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, kv_dtype="bf16", q_dtype="bf16", seed=93,
+                           context_lens=(300, 17, 1000)))
+    s = inp.spec
+    n_out = s.batch * s.num_q_heads * s.head_dim
+    guard = 256
+    out_big = torch.full((n_out + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+    out = out_big[guard:guard + n_out].view(s.batch, s.num_q_heads, s.head_dim)
+    dev = to_device(inp)
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+    pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
+    pool.set_partition_tokens(64)
+    nbytes = pool.workspace_bytes(s.num_q_heads)
+    pool.close()
+    ws_big = torch.full((nbytes + 2 * 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = ws_big[4096:4096 + nbytes]
+    say("[parity] canaries")
+    got = gpu_decode(inp, part_tokens=64, dev=dev, out=out, workspace=ws)
+    ob = out_big.cpu().numpy()
+    assert np.all(ob[:guard] == 12345.0) and np.all(ob[guard + n_out:] == 12345.0)
+    wb = ws_big.cpu().numpy()
+    assert np.all(wb[:4096] == 0xA5) and np.all(wb[4096 + nbytes:] == 0xA5)
+    assert max_err(got, oracle_decode(inp)) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# FP8: the hardware conversion of every finite code
+
+
+def test_fp8_every_code_round_trips():
+    """One token per sequence, unit scales: the output is exactly V's codes."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0, 0], np.uint8)
+    codes = codes.reshape(2, 128)
+    spec = Spec(name="codes", batch=2, num_q_heads=1, num_kv_heads=1, head_dim=128,
+                kv_dtype="fp8_e4m3", q_dtype="bf16", seed=94, context_lens=(1, 1))
+    inp = make_inputs(spec)
+    for b in range(2):
+        phys = inp.block_table[b, 0]
+        inp.v_pool[phys, 0, 0, :] = codes[b]
+        inp.v_scale[phys, 0, 0] = 1.0
+    say("[parity] fp8 codes")
+    got = gpu_decode(inp)
+    want = oracle.e4m3fn_to_f64(codes)
+    assert np.array_equal(got[:, 0, :].astype(np.float64), want)
+
+
+# ---------------------------------------------------------------------------
+# host utilities that touch the GPU
+
+
+def test_validate_tables():
+    inp = make_inputs(Spec(name="val", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                           kv_dtype="bf16", q_dtype="bf16", seed=95, context_lens=(40, 3)))
+    dev = to_device(inp)
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+    try:
+        pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
+        pa.pa_block_table_validate(pool.handle)
+        bad = dev.block_table.clone()
+        bad[0, 1] = inp.num_blocks + 3
+        pool.set_block_table(bad, dev.context_lens, inp.max_context_len)
+        with pytest.raises(pa.PAError) as ei:
+            pa.pa_block_table_validate(pool.handle)
+        assert ei.value.status == pa.binding.PA_ERR_SHAPE
+        pool.set_block_table(dev.block_table, dev.context_lens, 39)
+        with pytest.raises(pa.PAError):
+            pa.pa_block_table_validate(pool.handle)
+    finally:
+        pool.close()
+
+
+def test_profile_events():
+    inp = named("tiny_f32")
+    dev = to_device(inp)
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "f32")
+    try:
+        pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
+        ws = torch.empty(pool.workspace_bytes(8), dtype=torch.uint8, device="cuda")
+        out = torch.empty(2, 8, 64, device="cuda")
+        pa.pa_profile_enable(pool.handle, 4)
+        for _ in range(6):
+            pool.decode(dev.q, out, ws)
+        part, merge = pa.pa_profile_read(pool.handle, 8)
+        assert len(part) == 4 and all(t > 0 for t in part) and all(t > 0 for t in merge)
+        pa.pa_profile_enable(pool.handle, 0)
+    finally:
+        pool.close()

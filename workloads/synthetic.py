@@ -131,11 +131,12 @@ def _to_fp8(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     ``x``: float32 [n, 16, Hkv, d].  Returns codes uint8 [n, 16, Hkv, d]
     and scales float32 [n, Hkv, 16].
     """
-    amax = np.abs(x).max(axis=-1)  # [n, 16, Hkv]
-    sc = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
-    y = np.clip(x / sc[..., None], -FP8_MAX, FP8_MAX).astype(np.float32)
-    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    return codes, np.ascontiguousarray(sc.transpose(0, 2, 1))
+    xt = torch.from_numpy(x)
+    amax = xt.abs().amax(dim=-1)  # [n, 16, Hkv]
+    sc = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    y = (xt / sc[..., None]).clamp_(-FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, np.ascontiguousarray(sc.numpy().transpose(0, 2, 1))
 
 
 def _draw_pool(rng, n_blocks, hkv, d, kv_dtype, out_ch, gain, chunk_blocks):
