@@ -107,9 +107,10 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_b32_ctx4k")
-    ap.add_argument("--layers", type=int, default=4,
+    ap.add_argument("--layers", type=int, default=8,
                     help="independent KV pools cycled by the timed loop")
     ap.add_argument("--partition-tokens", type=int, default=0, help="0: automatic")
+    ap.add_argument("--heads-per-workgroup", type=int, default=0, help="0: automatic")
     ap.add_argument("--cold-iters", type=int, default=30,
                     help="extra steps timed after a 1 GiB cache flush each")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -147,8 +148,11 @@ def main():
         p.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
         if args.partition_tokens:
             p.set_partition_tokens(args.partition_tokens)
+        if args.heads_per_workgroup:
+            p.set_heads_per_workgroup(args.heads_per_workgroup)
         pools.append(p)
     part_tokens = pools[0].partition_tokens()
+    hc = pools[0].heads_per_workgroup()
     ws_bytes = pools[0].workspace_bytes(s.num_q_heads)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
@@ -160,22 +164,21 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    per_pool = (args.steps + R - 1) // R
-    for p in pools:
-        pa.pa_profile_enable(p.handle, per_pool)
-    log(f"timing {args.steps} steps (partition {part_tokens} tokens, {R} layers)")
+    # HIP events around the kernels of the steps that use pool 0 (every R-th
+    # step of the timed region): recording them on every step would itself
+    # add several microseconds between back-to-back launches.
+    n_prof = (args.steps + R - 1) // R
+    pa.pa_profile_enable(pools[0].handle, n_prof)
+    log(f"timing {args.steps} steps (partition {part_tokens} tokens, {hc} KV heads per "
+        f"workgroup, {R} layers cycled, events on every {R}-th step)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    part_ms, merge_ms = [], []
-    for p in pools:
-        a, b = pa.pa_profile_read(p.handle, per_pool)
-        part_ms += a
-        merge_ms += b
-        pa.pa_profile_enable(p.handle, 0)
+    part_ms, merge_ms = pa.pa_profile_read(pools[0].handle, n_prof)
+    pa.pa_profile_enable(pools[0].handle, 0)
     if not bool(torch.isfinite(out).all()):
         raise RuntimeError("non-finite output")
 
@@ -188,13 +191,15 @@ def main():
     log(f"{sec_per_step * 1e6:.1f} us/step, {tbs:.3f} TB/s; partition kernel "
         f"{part_avg * 1e6:.1f} us ({achieved:.0f} GB/s), merge {merge_avg * 1e6:.1f} us")
 
-    # cold steps: every step after writing 1 GiB elsewhere (flush outside the events)
+    # cold steps: every step after reading 1 GiB elsewhere, which evicts the
+    # KV from the caches without leaving dirty lines behind (flush outside
+    # the events)
     cold = []
     if args.cold_iters > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(args.cold_iters):
-            flush.fill_(float(i))
+            flush.sum()
             ev0.record()
             step(i)
             ev1.record()
@@ -236,14 +241,14 @@ def main():
             "context_tokens": int(inp.max_context_len), "block_size": 16,
             "kv_dtype": s.kv_dtype, "q_dtype": s.q_dtype, "out_dtype": "f32",
             "kv_bytes_per_step": nbytes, "partition_tokens": part_tokens,
-            "layers_cycled": R,
+            "layers_cycled": R, "kv_heads_per_workgroup": hc,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "partition_kernel", "kernel_us": round(part_avg * 1e6, 2),
-            "merge_us": round(merge_avg * 1e6, 2),
+            "merge_us": round(merge_avg * 1e6, 2) if ws_bytes else None,
         },
         "us_per_step": round(sec_per_step * 1e6, 2),
         "pct_of_hbm_peak": round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2),
@@ -251,7 +256,7 @@ def main():
             "median_step_us": round(statistics.median(cold) * 1e6, 2),
             "tb_s": round(nbytes / statistics.median(cold) / 1e12, 4),
             "iters": len(cold),
-            "note": "one step after writing 1 GiB elsewhere; event-timed step",
+            "note": "one step after reading 1 GiB elsewhere; event-timed step",
         },
         "cpu_baseline": cpu,
     }

@@ -190,6 +190,12 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
  * tokens: 0 restores the automatic choice; otherwise a multiple of 16 in
  * [16, 1 << 20].  Any value gives the same result up to rounding (the
  * merge is exact); it only changes parallelism and workspace size.
+ * Automatic choice: the whole context (one partition, no merge, no
+ * workspace) when batch * num_kv_heads / heads_per_workgroup >= 256;
+ * otherwise the longest context is cut into ceil(256 / that product)
+ * partitions.  The choice sees only max_context_len: for batches of very
+ * uneven lengths a caller that knows them may do better with a shorter
+ * partition (the grid then balances itself over the compute units).
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
  */
 pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens);
@@ -200,6 +206,27 @@ pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens);
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set).
  */
 pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens);
+
+/*
+ * pa_decode_set_heads_per_workgroup -- override how many adjacent KV heads
+ * one workgroup of the attention kernel takes.
+ *
+ * heads: 0 restores the automatic choice; otherwise a power of two that
+ * divides num_kv_heads and is at most the workgroup's wave count (4).  Any
+ * value gives the same result; it changes how many contiguous bytes of
+ * each block one workgroup reads and how many workgroups there are.
+ * Automatic choice: the largest chunk for which batch * num_kv_heads /
+ * heads still gives each of the 256 compute units a workgroup, else 1.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
+ */
+pa_status pa_decode_set_heads_per_workgroup(pa_kv_pool *pool, int32_t heads);
+
+/*
+ * pa_decode_heads_per_workgroup -- head chunk the next run will use for the
+ * table set last.
+ * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set).
+ */
+pa_status pa_decode_heads_per_workgroup(const pa_kv_pool *pool, int32_t *heads);
 
 /*
  * pa_profile_enable -- time the attention kernel of the next runs.

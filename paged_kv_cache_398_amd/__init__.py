@@ -15,8 +15,10 @@ from .binding import (  # noqa: F401
     pa_block_table_set,
     pa_block_table_validate,
     pa_decode_fp8_run,
+    pa_decode_heads_per_workgroup,
     pa_decode_partition_tokens,
     pa_decode_run,
+    pa_decode_set_heads_per_workgroup,
     pa_decode_set_partition_tokens,
     pa_decode_workspace_bytes,
     pa_kv_pool_create,
@@ -58,6 +60,12 @@ class PagedKVPool:
 
     def partition_tokens(self):
         return pa_decode_partition_tokens(self.handle)
+
+    def set_heads_per_workgroup(self, heads):
+        pa_decode_set_heads_per_workgroup(self.handle, heads)
+
+    def heads_per_workgroup(self):
+        return pa_decode_heads_per_workgroup(self.handle)
 
     def workspace_bytes(self, num_q_heads):
         return pa_decode_workspace_bytes(self.handle, num_q_heads)

@@ -34,6 +34,8 @@ SIGNATURES = [
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_set_partition_tokens", _i32, [_vp, _i32]),
     ("pa_decode_partition_tokens", _i32, [_vp, ctypes.POINTER(_i32)]),
+    ("pa_decode_set_heads_per_workgroup", _i32, [_vp, _i32]),
+    ("pa_decode_heads_per_workgroup", _i32, [_vp, ctypes.POINTER(_i32)]),
     ("pa_profile_enable", _i32, [_vp, _i32]),
     ("pa_profile_read", _i32, [_vp, ctypes.POINTER(_f32), ctypes.POINTER(_f32), _i32,
                                ctypes.POINTER(_i32)]),
@@ -153,6 +155,16 @@ def pa_decode_set_partition_tokens(pool, tokens) -> None:
 def pa_decode_partition_tokens(pool) -> int:
     t = _i32()
     _check(load_library().pa_decode_partition_tokens(pool, ctypes.byref(t)))
+    return t.value
+
+
+def pa_decode_set_heads_per_workgroup(pool, heads) -> None:
+    _check(load_library().pa_decode_set_heads_per_workgroup(pool, heads))
+
+
+def pa_decode_heads_per_workgroup(pool) -> int:
+    t = _i32()
+    _check(load_library().pa_decode_heads_per_workgroup(pool, ctypes.byref(t)))
     return t.value
 
 

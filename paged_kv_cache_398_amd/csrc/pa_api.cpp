@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -26,6 +27,7 @@ struct pa_kv_pool {
   const int32_t *block_table = nullptr, *context_lens = nullptr;
   int32_t batch = 0, max_blocks_per_seq = 0, max_context_len = 0;
   int32_t partition_override = 0;  // 0: automatic
+  int32_t heads_override = 0;      // 0: automatic
   // profiling
   int32_t prof_capacity = 0, prof_count = 0;
   std::vector<hipEvent_t> prof_events;  // 3 per run: before, between, after
@@ -60,40 +62,65 @@ int kind_of(pa_dtype t) {
   }
 }
 
-// MI355X: 256 compute units in 8 XCDs.  The partition choice (and so the
+// MI355X: 256 compute units in 8 XCDs.  The launch shape (and so the
 // workspace size) depends only on the arguments, never on a runtime query.
-constexpr int kComputeUnits = 256;
-constexpr int kTargetWorkgroupsPerCU = 4;
+constexpr int64_t kComputeUnits = 256;
+// Longest partition (tokens); keeps every token index of the kernels in int32.
+constexpr int32_t kMaxPartition = 1 << 20;
 
-// Tokens per context partition.  Each workgroup (kWaves waves) takes one
-// partition of one (sequence, KV head); waves take whole 16-token blocks.
-// Prefer long partitions (fewer partial results to merge) as long as the
-// grid still offers kTargetWorkgroupsPerCU workgroups per compute unit.
-int32_t auto_partition_tokens(const pa_kv_pool *p) {
-  const int64_t units = (int64_t)p->batch * p->num_kv_heads;
-  const int64_t target = (int64_t)kTargetWorkgroupsPerCU * kComputeUnits;
-  const int64_t ctx = p->max_context_len;
-  for (int bpw = 64; bpw >= 1; bpw /= 2) {  // blocks per wave
-    const int64_t tokens = (int64_t)bpw * PA_BLOCK_SIZE * pa::kWaves;
-    if (units * ((ctx + tokens - 1) / tokens) >= target) return (int32_t)tokens;
-  }
-  return PA_BLOCK_SIZE * pa::kWaves;
+// Largest head chunk a workgroup may take: a power of two dividing both
+// num_kv_heads and kWaves (each wave works on one head of the chunk).
+int32_t max_heads_per_workgroup(int32_t hkv) {
+  int32_t hc = 1;
+  while (hc * 2 <= pa::kWaves && hkv % (hc * 2) == 0) hc *= 2;
+  return hc;
 }
 
+// KV heads per workgroup.  Automatic choice: the largest chunk that still
+// gives every compute unit a (sequence, chunk) of its own, so that contexts
+// need not be split (no partial results, no merge); wider chunks read
+// longer contiguous runs of each block.  When even single heads are too few
+// the contexts must be split anyway, and then the widest chunk is best.
+int32_t heads_per_workgroup(const pa_kv_pool *p) {
+  if (p->heads_override > 0) return p->heads_override;
+  const int32_t hmax = max_heads_per_workgroup(p->num_kv_heads);
+  for (int32_t hc = hmax; hc >= 1; hc /= 2)
+    if ((int64_t)p->batch * (p->num_kv_heads / hc) >= kComputeUnits) return hc;
+  return hmax;
+}
+
+// Tokens per context partition (a multiple of 16).  Automatic choice: the
+// whole context when the (sequence, chunk) pairs already cover the compute
+// units (no partial results, no merge); otherwise the context is cut into
+// as many partitions as it takes to give each compute unit a workgroup.
 int32_t partition_tokens(const pa_kv_pool *p) {
-  return p->partition_override > 0 ? p->partition_override : auto_partition_tokens(p);
+  if (p->partition_override > 0) return p->partition_override;
+  const int64_t units = (int64_t)p->batch * (p->num_kv_heads / heads_per_workgroup(p));
+  const int64_t parts = units >= kComputeUnits ? 1 : (kComputeUnits + units - 1) / std::max<int64_t>(units, 1);
+  // whole context: rounded up to a block; split: rounded down, so that the
+  // split gives at least `parts` partitions
+  const int64_t ctx = p->max_context_len;
+  const int64_t tokens = parts == 1 ? (ctx + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE * PA_BLOCK_SIZE
+                                    : ctx / parts / PA_BLOCK_SIZE * PA_BLOCK_SIZE;
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(tokens, PA_BLOCK_SIZE), kMaxPartition);
 }
 
 struct Layout {
-  int32_t part_tokens, parts;
+  int32_t part_tokens, parts, hc, chunks;
   size_t ml_bytes, acc_offset, total;
 };
 
 Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
   Layout L{};
   L.part_tokens = partition_tokens(p);
-  L.parts = (int32_t)((p->max_context_len + (int64_t)L.part_tokens - 1) / L.part_tokens);
-  const size_t recs = (size_t)p->batch * hq * L.parts;
+  // at least one partition: its workgroups also write the zero rows of
+  // empty sequences
+  L.parts = (int32_t)std::max<int64_t>(
+      1, (p->max_context_len + (int64_t)L.part_tokens - 1) / L.part_tokens);
+  L.hc = heads_per_workgroup(p);
+  L.chunks = p->num_kv_heads / L.hc;
+  // a single partition writes the output directly; no partials to keep
+  const size_t recs = L.parts > 1 ? (size_t)p->batch * hq * L.parts : 0;
   L.ml_bytes = recs * sizeof(float2);
   L.acc_offset = (L.ml_bytes + 255) & ~(size_t)255;
   L.total = recs ? L.acc_offset + recs * p->head_dim * sizeof(float) : 0;
@@ -129,12 +156,14 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
     if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   }
-  const size_t wgs = (size_t)pool->batch * pool->num_kv_heads * L.parts;
+  const size_t wgs = (size_t)pool->batch * L.chunks * L.parts;
   if (wgs * pa::kWaves * 64 >= (size_t(1) << 32) || (size_t)pool->batch * hq >= (size_t(1) << 31))
     return fail(PA_ERR_SHAPE, "launch grid too large (raise the partition length)");
   if (pool->batch == 0) return ok();
 
   // ---- from here on HIP is used
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
   pa::LaunchArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
@@ -155,13 +184,13 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   a.max_ctx = pool->max_context_len;
   a.part_tokens = L.part_tokens;
   a.parts = L.parts;
+  a.hc = L.hc;
+  a.chunks = L.chunks;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.kv = kind_of(pool->kv_dtype);
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool prof = pool->prof_capacity > 0 && pool->prof_count < pool->prof_capacity;
   hipEvent_t *ev = prof ? &pool->prof_events[3 * (size_t)pool->prof_count] : nullptr;
-  hipError_t e = hipSuccess;
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess)
     return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   if ((e = pa::launch_partition(a, s)) != hipSuccess)
@@ -308,7 +337,7 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
 
 pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
-  if (tokens != 0 && (tokens < PA_BLOCK_SIZE || tokens % PA_BLOCK_SIZE || tokens > (1 << 20)))
+  if (tokens != 0 && (tokens < PA_BLOCK_SIZE || tokens % PA_BLOCK_SIZE || tokens > kMaxPartition))
     return fail(PA_ERR_SHAPE, "partition length %d: 0 or a multiple of 16 in [16, 2^20]", tokens);
   pool->partition_override = tokens;
   return ok();
@@ -318,6 +347,23 @@ pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens) {
   if (!pool || !tokens) return fail(PA_ERR_NULL, "pool or tokens is NULL");
   if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set");
   *tokens = partition_tokens(pool);
+  return ok();
+}
+
+pa_status pa_decode_set_heads_per_workgroup(pa_kv_pool *pool, int32_t heads) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  const int32_t hmax = max_heads_per_workgroup(pool->num_kv_heads);
+  if (heads != 0 && (heads < 1 || heads > hmax || (heads & (heads - 1))))
+    return fail(PA_ERR_SHAPE, "heads per workgroup %d: 0 or a power of two dividing %d, at most %d",
+                heads, pool->num_kv_heads, hmax);
+  pool->heads_override = heads;
+  return ok();
+}
+
+pa_status pa_decode_heads_per_workgroup(const pa_kv_pool *pool, int32_t *heads) {
+  if (!pool || !heads) return fail(PA_ERR_NULL, "pool or heads is NULL");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set");
+  *heads = heads_per_workgroup(pool);
   return ok();
 }
 

@@ -5,13 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef PA_WAVES
+#define PA_WAVES 4
+#endif
+
 namespace pa {
 
 enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
-// Waves per workgroup of the partition kernel.  The blocks of one partition
-// are dealt round-robin to the waves.
-constexpr int kWaves = 4;
+// Waves per workgroup of the attention kernel.  A workgroup owns one context
+// partition of one sequence for a chunk of `hc` KV heads; wave w works on
+// head w % hc of the chunk and takes every (kWaves / hc)-th block of the
+// partition, so the workgroup as a whole streams whole physical blocks.
+constexpr int kWaves = PA_WAVES;
+static_assert(kWaves == 4 || kWaves == 8 || kWaves == 16, "4, 8 or 16 waves");
 
 // Everything one decode launch needs; plain pointers into device memory.
 struct LaunchArgs {
@@ -28,6 +35,8 @@ struct LaunchArgs {
   int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx;
   int32_t part_tokens;      // tokens per partition (multiple of 16)
   int32_t parts;            // ceil(max_ctx / part_tokens)
+  int32_t hc;               // KV heads per workgroup (divides hkv and kWaves)
+  int32_t chunks;           // hkv / hc
   float scale_log2e;        // softmax scale * log2(e)
   int kv;                   // KvKind
 };
@@ -35,10 +44,11 @@ struct LaunchArgs {
 // True when a kernel is built for (kv, head_dim, group size).
 bool kernel_supported(int kv, int d, int group);
 
-// Enqueue the partition kernel (grid batch*hkv*parts workgroups).
+// Enqueue the attention kernel (grid batch * chunks * parts workgroups).
 hipError_t launch_partition(const LaunchArgs &a, hipStream_t stream);
 
-// Enqueue the log-sum-exp merge kernel (grid batch*hq workgroups).
+// Enqueue the log-sum-exp merge kernel (grid batch * hq workgroups); a no-op
+// when there is a single partition (the attention kernel then writes out).
 hipError_t launch_merge(const LaunchArgs &a, hipStream_t stream);
 
 }  // namespace pa

@@ -8,33 +8,40 @@
 // 与三路省内存方案", sections 一, 三 and 六; grouping of query heads as in the
 // GQA section of "大模型推理为何这么慢？从内存带宽瓶颈到KV Cache优化的技术突围").
 //
-// How (two kernels, always both):
+// How:
 //
-// 1. partition_kernel: one workgroup of kWaves waves per (sequence, KV head,
-//    context partition).  The partition's 16-token blocks are dealt
-//    round-robin to the waves.  A wave reads a whole block per step: each
-//    token row (head_dim elements of one KV head) is split over LPT lanes,
-//    64/LPT tokens per pass, 16/LPT*4 passes per block, with 8- or 16-byte
-//    loads per lane so every load instruction reads whole 64-256 B row
-//    segments.  Every K/V element is loaded from HBM once and used by all G
-//    query heads of its group, which sit in the same lane's registers.
+// 1. partition_kernel: one workgroup of kWaves waves per (sequence, chunk of
+//    hc adjacent KV heads, context partition).  Wave w works on head
+//    w % hc of the chunk and takes every (kWaves/hc)-th 16-token block of the
+//    partition, so the workgroup as a whole reads the hc heads' rows of
+//    every block it touches: hc * head_dim * elem bytes contiguous per token.
+//    A wave holds a whole block of its head in registers: each token row is
+//    split over LPT lanes, 64/LPT tokens per pass, with 8- or 16-byte loads
+//    per lane.  Every K/V element is loaded from HBM once and used by all G
+//    query heads of its group, which sit in the same lane's registers.  The
+//    loop is a two-stage software pipeline: the next block's loads are in
+//    flight while the current block is computed, and the block table of up
+//    to 64 blocks is read by one vector load before it starts.
 //    Scores are reduced over the LPT lanes of a token with DPP.  The
 //    softmax is accumulated online (running max and sum, as in the
 //    FlashAttention sections of the pages): the running max is kept
 //    wave-uniform and is only raised when a block's maximum exceeds it by
 //    more than kTau (log2 units), so the rescale of the accumulators is
 //    rare; any running max gives the same normalised result, it only bounds
-//    the exponentials (by 2^kTau).  At the end the lanes' and waves' states
-//    are combined exactly and written as (max, sum, unnormalised output).
+//    the exponentials (by 2^kTau).  At the end the lanes' states and the
+//    phases of each head are combined exactly in LDS.  With one partition
+//    the normalised output is written directly; otherwise (max, sum,
+//    unnormalised output) per query head and partition.
 //
-// 2. merge_kernel: one wave per (sequence, query head) combines the
-//    partitions: M = max_p m_p, w_p = 2^(m_p - M), out = sum w_p acc_p /
-//    sum w_p l_p.
+// 2. merge_kernel (only with several partitions): one workgroup per
+//    (sequence, query head) combines the partitions: M = max_p m_p,
+//    w_p = 2^(m_p - M), out = sum w_p acc_p / sum w_p l_p.
 //
 // Positions past a sequence's length contribute exactly nothing (selects,
 // not multiplications, so NaN garbage in unused slots cannot leak), table
 // entries past the last used block are never read, and block ids outside
-// [0, num_blocks) are skipped rather than dereferenced.
+// [0, num_blocks) are never dereferenced: block 0 is read in their place and
+// masked out.
 
 #include "pa_internal.h"
 
@@ -49,16 +56,22 @@ __host__ __device__ constexpr int elem_bytes(int kv) {
   return kv == KV_F32 ? 4 : (kv == KV_BF16 ? 2 : 1);
 }
 
+#ifndef PA_ACC_REGS
+#define PA_ACC_REGS 64
+#endif
 // Lanes per token row: as few as possible while keeping the per-lane output
-// accumulators (G * D / LPT floats) at 64 registers or fewer.
-__host__ __device__ constexpr int lanes_per_token(int d, int g) {
-  return (g * d / 4 <= 64) ? 4 : ((g * d / 8 <= 64) ? 8 : 16);
+// accumulators (G * D / LPT floats) at PA_ACC_REGS registers or fewer, and
+// each lane's slice of a row at 8 bytes or more.
+__host__ __device__ constexpr int lanes_per_token(int d, int g, int eb) {
+  int l = (g * d / 4 <= PA_ACC_REGS) ? 4 : ((g * d / 8 <= PA_ACC_REGS) ? 8 : 16);
+  while (l > 4 && d * eb / l < 8) l /= 2;
+  return l;
 }
 
 template <int KV, int D, int G>
 struct Cfg {
   static constexpr int EB = elem_bytes(KV);
-  static constexpr int LPT = lanes_per_token(D, G);
+  static constexpr int LPT = lanes_per_token(D, G, EB);
   static constexpr int ROW = D * EB;               // bytes of one token row (one head)
   static constexpr int LB = ROW / LPT;             // bytes per lane per token
   static constexpr int CH = LB < 16 ? LB : 16;     // bytes per load instruction
@@ -152,7 +165,7 @@ __device__ __forceinline__ void to_float(const uint32_t *r, float *f) {
 }
 
 // ---------------------------------------------------------------------------
-// partition kernel
+// attention kernel
 
 template <int KV, int D, int G>
 struct Block {  // one block's K/V slice held by one lane
@@ -169,26 +182,40 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
   using C = Cfg<KV, D, G>;
   constexpr int LPT = C::LPT, NPASS = C::NPASS, DW = C::DW, EPL = C::EPL;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // wave index, known wave-uniform: everything derived from it stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LPT;   // which slice of the row
   const int slot = lane / LPT;  // which token of the pass
 
+  // workgroup -> (sequence, head chunk, partition); partitions fastest
   int u = blockIdx.x;
-  const int g = u % a.hkv;
-  u /= a.hkv;
-  const int b = u % a.batch;
-  const int part = u / a.batch;
+  const int part = u % a.parts;
+  u /= a.parts;
+  const int chunk = u % a.chunks;
+  const int b = u / a.chunks;
+  // wave -> (KV head of the chunk, phase); the phases of a head split its blocks
+  const int hc = a.hc;
+  const int nph = kWaves / hc;
+  const int hl = w % hc;
+  const int ph = w / hc;
+  const int g = chunk * hc + hl;
+  const int h0 = g * G;  // first query head of this wave's group
 
   const int n = min(max(a.ctx[b], 0), a.max_ctx);
   const int tok0 = part * a.part_tokens;
-  if (tok0 >= n) return;  // whole workgroup: nothing of this sequence here
+  if (tok0 >= n) {  // whole workgroup: nothing of this sequence here
+    if (part == 0) {  // empty sequence: its output rows are zero
+      for (int idx = threadIdx.x; idx < hc * G * D; idx += kThreads)
+        a.out[((size_t)b * a.hq + chunk * hc * G) * D + idx] = 0.f;
+    }
+    return;
+  }
   const int tok_end = min(n, tok0 + a.part_tokens);
   const int blk0 = tok0 / kBlock;
   const int nblk = (tok_end - tok0 + kBlock - 1) / kBlock;
-  const int nb_w = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
+  const int nb_w = nblk > ph ? (nblk - ph + nph - 1) / nph : 0;
 
   // ---- query slice of the G heads of this group (lane-local elements)
-  const int h0 = g * G;
   float qf[G][EPL];
   uint32_t q2[G][DW];  // bf16 pairs (bf16 pools only)
 #pragma unroll
@@ -217,35 +244,34 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
 
   // ---- lane offsets inside a block, and the block table of this wave
   const size_t block_bytes = (size_t)kBlock * a.hkv * C::ROW;
-  int lane_off[NPASS];
+  uint32_t lane_off[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p)
-    lane_off[p] = ((p * C::TPP + slot) * a.hkv + g) * C::ROW + sub * C::CH;
-  const int *trow = a.table + (size_t)b * a.max_blocks + blk0 + w;  // i-th block: trow[i*kWaves]
+    lane_off[p] = (uint32_t)(((p * C::TPP + slot) * a.hkv + g) * C::ROW + sub * C::CH);
+  // i-th block of this wave: table entry trow[i * nph]
+  const int *trow = a.table + (size_t)b * a.max_blocks + blk0 + ph;
   const char *kbase = static_cast<const char *>(a.k_cache);
   const char *vbase = static_cast<const char *>(a.v_cache);
-  int tv = -1;  // lane j holds the id of this wave's block (i & ~63) + j
 
-  auto issue = [&](Block<KV, D, G> &bk, int i) {
-    if ((i & 63) == 0) {
-      const int idx = i + lane;
-      tv = idx < nb_w ? trow[(size_t)idx * kWaves] : -1;
-    }
-    const int phys = __builtin_amdgcn_readlane(tv, i & 63);
-    bk.tok = (blk0 + w + i * kWaves) * kBlock;
+  // Loads of a block are issued unconditionally (an id outside the pool is
+  // replaced by block 0 and the block masked in compute), so the loop below
+  // has no branch around a load and the next block's loads stay in flight
+  // while the current block is computed.
+  auto issue = [&](Block<KV, D, G> &bk, int i, int phys) {
+    bk.tok = (blk0 + ph + i * nph) * kBlock;
     bk.ok = (unsigned)phys < (unsigned)a.num_blocks;
-    if (!bk.ok) return;
-    const char *kb = kbase + (size_t)phys * block_bytes;
-    const char *vb = vbase + (size_t)phys * block_bytes;
+    const size_t boff = bk.ok ? (size_t)phys * block_bytes : 0;
+    const char *kb = kbase + boff;  // wave-uniform base, 32-bit lane offsets
+    const char *vb = vbase + boff;
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
 #pragma unroll
       for (int c = 0; c < C::NCH; ++c) {
-        load_chunk<C::CH>(kb + lane_off[p] + c * LPT * C::CH, &bk.k[p][c * (C::CH / 4)]);
-        load_chunk<C::CH>(vb + lane_off[p] + c * LPT * C::CH, &bk.v[p][c * (C::CH / 4)]);
+        load_chunk<C::CH>(kb + (lane_off[p] + c * LPT * C::CH), &bk.k[p][c * (C::CH / 4)]);
+        load_chunk<C::CH>(vb + (lane_off[p] + c * LPT * C::CH), &bk.v[p][c * (C::CH / 4)]);
       }
       if constexpr (KV == KV_FP8) {
-        const size_t si = ((size_t)phys * a.hkv + g) * kBlock + p * C::TPP + slot;
+        const size_t si = ((bk.ok ? (size_t)phys : 0) * a.hkv + g) * kBlock + p * C::TPP + slot;
         bk.ks[p] = a.k_scale[si];
         bk.vs[p] = a.v_scale[si];
       }
@@ -264,13 +290,13 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
   const float sl2 = a.scale_log2e;
 
   auto compute = [&](const Block<KV, D, G> &bk) {
-    if (!bk.ok) return;
-    const bool tail = bk.tok + kBlock > tok_end;  // wave-uniform
+    // a partial last block, or a block id outside the pool: mask slots
+    const bool tail = !bk.ok || bk.tok + kBlock > tok_end;  // wave-uniform
     float s[NPASS][G];
     bool live[NPASS];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      live[p] = !tail || (bk.tok + p * C::TPP + slot < tok_end);
+      live[p] = !tail || (bk.ok && bk.tok + p * C::TPP + slot < tok_end);
       float kf[EPL];
       if constexpr (KV != KV_BF16) to_float<KV, DW, EPL>(bk.k[p], kf);
 #pragma unroll
@@ -338,21 +364,39 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
     }
   };
 
-  // ---- main loop, one block in flight while the previous is computed
-  {
+  // ---- main loop: a two-stage pipeline over the wave's blocks, block i+1 in
+  // flight while block i is computed.  The table entries of up to 64 blocks
+  // are fetched by one vector load (lane j holds block c0 + j) before the
+  // pipeline starts, so the loop itself reads nothing but K and V.
+  for (int c0 = 0; c0 < nb_w; c0 += 64) {
+    const int cn = min(64, nb_w - c0);
+    const int tv = c0 + lane < nb_w ? trow[(size_t)(c0 + lane) * nph] : -1;
+    auto entry = [&](int i) { return __builtin_amdgcn_readlane(tv, min(i, cn - 1)); };
     Block<KV, D, G> A, B;
-    if (nb_w > 0) issue(A, 0);
-    for (int i = 0; i < nb_w; i += 2) {
-      if (i + 1 < nb_w) issue(B, i + 1);
+    issue(A, c0, entry(0));
+    // The scheduling barriers keep the next block's loads ahead of the
+    // first use of the current block; without them the compiler sinks the
+    // loads below that use and the two blocks are fetched one after another.
+    int i = 0;
+    for (; i + 2 < cn; i += 2) {
+      issue(B, c0 + i + 1, entry(i + 1));
+      __builtin_amdgcn_sched_barrier(0);
       compute(A);
-      if (i + 1 < nb_w) {
-        if (i + 2 < nb_w) issue(A, i + 2);
-        compute(B);
-      }
+      issue(A, c0 + i + 2, entry(i + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B);
+    }
+    if (i + 1 < cn) {
+      issue(B, c0 + i + 1, entry(i + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A);
+      compute(B);
+    } else {
+      compute(A);
     }
   }
 
-  // ---- combine the wave's token slots, then the waves, exactly
+  // ---- combine the wave's token slots, then the phases of each head, exactly
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     l[hh] = slot_reduce<LPT, false>(l[hh]);
@@ -378,63 +422,127 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int hh = idx / D, e = idx % D;
-    float M = s_m[0][hh];
-#pragma unroll
-    for (int v = 1; v < kWaves; ++v) M = fmaxf(M, s_m[v][hh]);
+  // outputs of this workgroup: hc heads x G query rows x D, query heads
+  // chunk*hc*G .. (chunk+1)*hc*G - 1 of sequence b
+  const size_t bh0 = (size_t)b * a.hq + (size_t)chunk * hc * G;
+  for (int idx = threadIdx.x; idx < hc * G * D; idx += kThreads) {
+    const int r = idx / D, e = idx % D;  // r = hl * G + hh
+    const int hh = r % G, hw = r / G;
+    float M = -__builtin_huge_valf();
+    for (int v = 0; v < nph; ++v) M = fmaxf(M, s_m[v * hc + hw][hh]);
     float A = 0.f, L = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float mv = s_m[v][hh];
+    for (int v = 0; v < nph; ++v) {
+      const int wv = v * hc + hw;
+      const float mv = s_m[wv][hh];
       const float sc = mv == -__builtin_huge_valf() ? 0.f : fast_exp2(mv - M);
-      A = fmaf(sc, s_acc[v][hh][e], A);
-      L = fmaf(sc, s_l[v][hh], L);
+      A = fmaf(sc, s_acc[wv][hh][e], A);
+      L = fmaf(sc, s_l[wv][hh], L);
     }
-    const size_t rec = ((size_t)b * a.hq + h0 + hh) * a.parts + part;
-    a.ws_acc[rec * D + e] = A;
-    if (e == 0) a.ws_ml[rec] = make_float2(M, L);
+    if (a.parts == 1) {
+      a.out[(bh0 + r) * D + e] = L > 0.f ? A / L : 0.f;
+    } else {
+      const size_t rec = (bh0 + r) * a.parts + part;
+      a.ws_acc[rec * D + e] = A;
+      if (e == 0) a.ws_ml[rec] = make_float2(M, L);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// merge kernel: one wave per (sequence, query head)
+// merge kernel: one workgroup of kMergeThreads per (sequence, query head)
+//
+// M = max_p m_p; w_p = 2^(m_p - M) (0 for a partition that saw no valid
+// token); out = sum_p w_p acc_p / sum_p w_p l_p.  The partitions are spread
+// over the workgroup: thread t takes columns 4*(t % (D/4)) .. +3 of every
+// (kMergeThreads / (D/4))-th partition, with four partitions' loads in flight.
+
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float x, float *scratch, bool is_max) {
+  // wave reduction (every lane ends with the result), then across waves
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) {
+    const float y = __shfl_xor(x, off);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) scratch[w] = x;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
+  __syncthreads();
+  return r;
+}
 
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(LaunchArgs a) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(LaunchArgs a) {
+  constexpr int C4 = D / 4;                    // float4 columns of a row
+  constexpr int NG = kMergeThreads / C4;       // partition groups
   const size_t bh = blockIdx.x;
   const int b = (int)(bh / a.hq);
   const int n = min(max(a.ctx[b], 0), a.max_ctx);
   const int np = (n + a.part_tokens - 1) / a.part_tokens;
   float *o = a.out + bh * D;
   if (np == 0) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[lane + 64 * k] = 0.f;
+    for (int e = threadIdx.x; e < D; e += kMergeThreads) o[e] = 0.f;
     return;
   }
   const float2 *ml = a.ws_ml + bh * a.parts;
-  const float *acc = a.ws_acc + bh * a.parts * D;
-  float M = -__builtin_huge_valf();
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[p].x);
-  float L = 0.f, A[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) A[k] = 0.f;
-  for (int p = 0; p < np; ++p) {
+  const float4 *acc4 = reinterpret_cast<const float4 *>(a.ws_acc + bh * a.parts * D);
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float4 s_part[NG][C4];
+
+  float mx = -__builtin_huge_valf();
+  for (int p = threadIdx.x; p < np; p += kMergeThreads) mx = fmaxf(mx, ml[p].x);
+  const float M = block_reduce(mx, s_red, true);
+  const auto weight = [&](float m) { return m == -__builtin_huge_valf() ? 0.f : fast_exp2(m - M); };
+  float lw = 0.f;
+  for (int p = threadIdx.x; p < np; p += kMergeThreads) {
     const float2 v = ml[p];
-    const float sc = v.x == -__builtin_huge_valf() ? 0.f : fast_exp2(v.x - M);
-    L = fmaf(sc, v.y, L);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) A[k] = fmaf(sc, acc[(size_t)p * D + lane + 64 * k], A[k]);
+    lw = fmaf(weight(v.x), v.y, lw);
   }
+  const float L = block_reduce(lw, s_red, false);
+
+  const int c = threadIdx.x % C4, grp = threadIdx.x / C4;
+  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float w, float4 v) {
+    A.x = fmaf(w, v.x, A.x); A.y = fmaf(w, v.y, A.y);
+    A.z = fmaf(w, v.z, A.z); A.w = fmaf(w, v.w, A.w);
+  };
+  int p = grp;
+  for (; p + 3 * NG < np; p += 4 * NG) {
+    float4 v[4];
+    float w[4];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[lane + 64 * k] = L > 0.f ? A[k] / L : 0.f;
+    for (int k = 0; k < 4; ++k) {
+      v[k] = acc4[(size_t)(p + k * NG) * C4 + c];
+      w[k] = ml[p + k * NG].x;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add(weight(w[k]), v[k]);
+  }
+  for (; p < np; p += NG) add(weight(ml[p].x), acc4[(size_t)p * C4 + c]);
+  s_part[grp][c] = A;
+  __syncthreads();
+  if (threadIdx.x < C4) {
+    float4 t = s_part[0][threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+      const float4 u = s_part[g][threadIdx.x];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    float *oo = o + 4 * threadIdx.x;  // out needs only 4-byte alignment
+    oo[0] = L > 0.f ? t.x / L : 0.f;
+    oo[1] = L > 0.f ? t.y / L : 0.f;
+    oo[2] = L > 0.f ? t.z / L : 0.f;
+    oo[3] = L > 0.f ? t.w / L : 0.f;
+  }
 }
 
 template <int KV, int D, int G>
 hipError_t launch_partition_t(const LaunchArgs &a, hipStream_t s) {
-  const size_t wgs = (size_t)a.batch * a.hkv * a.parts;
+  const size_t wgs = (size_t)a.batch * a.chunks * a.parts;
   hipLaunchKernelGGL((partition_kernel<KV, D, G>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -477,12 +585,12 @@ hipError_t launch_partition(const LaunchArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const LaunchArgs &a, hipStream_t s) {
-  if (a.batch == 0) return hipSuccess;
+  if (a.batch == 0 || a.parts <= 1) return hipSuccess;
   const unsigned wgs = (unsigned)((size_t)a.batch * a.hq);
   if (a.d == 64)
-    hipLaunchKernelGGL((merge_kernel<64>), dim3(wgs), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<64>), dim3(wgs), dim3(kMergeThreads), 0, s, a);
   else if (a.d == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), dim3(wgs), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<128>), dim3(wgs), dim3(kMergeThreads), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

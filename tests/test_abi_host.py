@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -83,6 +83,7 @@ def test_run_errors(pool):
     assert _status(run, pool, Q, "bf16", 8, 0.1, OUT, WS, 1 << 20, 0) == pa.binding.PA_ERR_STATE
     assert _status(pa.pa_decode_workspace_bytes, pool, 8) == pa.binding.PA_ERR_STATE
     pa.pa_block_table_set(pool, TBL, CTX, 3, 4, 64)
+    pa.pa_decode_set_partition_tokens(pool, 16)  # several partitions: partials to keep
     ws = pa.pa_decode_workspace_bytes(pool, 8)
     assert ws > 0
     assert _status(run, pool, Q, "f32", 8, 0.1, OUT, WS, ws, 0) == pa.binding.PA_ERR_DTYPE
@@ -129,21 +130,68 @@ def test_partition_override_and_workspace_size(pool):
     assert pa.pa_decode_workspace_bytes(pool, 8) == ml + recs * 128 * 4
     pa.pa_decode_set_partition_tokens(pool, 0)
     auto = pa.pa_decode_partition_tokens(pool)
-    assert auto % 64 == 0 and auto >= 64
+    assert auto % 16 == 0 and auto >= 16
+    # one partition writes the output directly: no workspace
+    pa.pa_decode_set_partition_tokens(pool, 1024)
+    assert pa.pa_decode_workspace_bytes(pool, 8) == 0
+    pa.pa_decode_set_partition_tokens(pool, 0)
     # an empty context needs no workspace
     pa.pa_block_table_set(pool, TBL, CTX, 3, 64, 0)
     assert pa.pa_decode_workspace_bytes(pool, 8) == 0
 
 
-def test_auto_partition_fills_the_chip(pool):
-    """The automatic partition gives >= 1024 workgroups when the work allows."""
-    for batch, ctx in [(32, 4096), (4, 131072), (64, 16384), (1, 512)]:
-        h = pa.pa_kv_pool_create(64, 16, 8, 128, "bf16", K, V)
-        pa.pa_block_table_set(h, TBL, CTX, batch, (ctx + 15) // 16, ctx)
-        p = pa.pa_decode_partition_tokens(h)
-        wgs = batch * 8 * -(-ctx // p)
-        assert wgs >= 1024 or p == 64, (batch, ctx, p)
-        pa.pa_kv_pool_destroy(h)
+WAVES_PER_WG = 4  # PA_WAVES of the default build
+CUS = 256
+
+
+def expected_shape(hkv, batch, ctx):
+    """The documented automatic launch shape, restated."""
+    hmax = max(c for c in (1, 2, 4) if c <= WAVES_PER_WG and hkv % c == 0)
+    fits = [c for c in (4, 2, 1) if c <= hmax and hkv % c == 0 and batch * (hkv // c) >= CUS]
+    hc = fits[0] if fits else hmax
+    units = batch * (hkv // hc)
+    parts = 1 if units >= CUS else -(-CUS // units)
+    tokens = -(-ctx // 16) * 16 if parts == 1 else ctx // parts // 16 * 16
+    return hc, min(max(tokens, 16), 1 << 20)
+
+
+def test_auto_launch_shape():
+    """One workgroup per compute unit at least; whole contexts when the
+    (sequence, head chunk) pairs already cover the compute units."""
+    cases = [(8, 32, 4096), (8, 4, 131072), (8, 64, 16384), (8, 1, 512), (32, 32, 8192),
+             (2, 2, 100), (1, 1, 100000), (8, 64, 0), (6, 100, 1000), (4, 128, 5000)]
+    for hkv, batch, ctx in cases:
+        h = pa.pa_kv_pool_create(64, 16, hkv, 128, "bf16", K, V)
+        try:
+            pa.pa_block_table_set(h, TBL, CTX, batch, max(1, (ctx + 15) // 16), ctx)
+            hc = pa.pa_decode_heads_per_workgroup(h)
+            p = pa.pa_decode_partition_tokens(h)
+            assert (hc, p) == expected_shape(hkv, batch, ctx), (hkv, batch, ctx, hc, p)
+            parts = max(1, -(-ctx // p))
+            assert batch * (hkv // hc) * parts >= min(CUS, batch * (hkv // hc) * -(-ctx // 16))
+            if batch * (hkv // hc) >= CUS:
+                assert parts == 1 and pa.pa_decode_workspace_bytes(h, hkv) == 0
+        finally:
+            pa.pa_kv_pool_destroy(h)
+    # one workgroup per (sequence, KV head), whole contexts
+    assert expected_shape(8, 32, 4096) == (1, 4096)
+    # four heads per workgroup, whole contexts
+    assert expected_shape(32, 32, 8192) == (4, 8192)
+    # too few sequences: widest chunk, 32 partitions of 4096 tokens
+    assert expected_shape(8, 4, 131072) == (4, 4096)
+
+
+def test_heads_override(pool):
+    pa.pa_block_table_set(pool, TBL, CTX, 3, 64, 1000)
+    assert _status(pa.pa_decode_set_heads_per_workgroup, pool, 3) == pa.binding.PA_ERR_SHAPE
+    assert _status(pa.pa_decode_set_heads_per_workgroup, pool, 4) == pa.binding.PA_ERR_SHAPE
+    assert _status(pa.pa_decode_set_heads_per_workgroup, pool, -1) == pa.binding.PA_ERR_SHAPE
+    pa.pa_decode_set_heads_per_workgroup(pool, 2)
+    assert pa.pa_decode_heads_per_workgroup(pool) == 2
+    pa.pa_decode_set_heads_per_workgroup(pool, 1)
+    assert pa.pa_decode_heads_per_workgroup(pool) == 1
+    pa.pa_decode_set_heads_per_workgroup(pool, 0)
+    assert pa.pa_decode_heads_per_workgroup(pool) == 2  # batch 3: split, widest chunk
 
 
 def test_profile_needs_enable(pool):

@@ -288,3 +288,36 @@ def test_profile_events():
         pa.pa_profile_enable(pool.handle, 0)
     finally:
         pool.close()
+
+
+# ---------------------------------------------------------------------------
+# the fused merge keeps its arrival counters consistent across runs
+
+
+def test_repeated_runs_on_one_handle():
+    """Runs on one handle reuse its arrival counters: every run must agree
+    with the oracle, also after a run with a smaller batch and after a run
+    whose partials go through the separate merge kernel."""
+    spec = Spec(name="repeat", batch=5, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                kv_dtype="bf16", q_dtype="bf16", seed=96, context_lens=(900, 17, 512, 0, 1300))
+    inp = make_inputs(spec, poison=True)
+    want = oracle_decode(inp)
+    dev = to_device(inp)
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+    try:
+        s = inp.spec
+        ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+        out = torch.empty((s.batch, s.num_q_heads, s.head_dim), device="cuda")
+        for it, (part, nb) in enumerate([(64, 5), (64, 5), (128, 3), (64, 5), (16, 5),
+                                         (64, 5), (0, 5), (64, 5)]):
+            say(f"[parity] repeat it={it} part={part} batch={nb}")
+            pool.set_block_table(dev.block_table[:nb], dev.context_lens[:nb], inp.max_context_len)
+            pool.set_partition_tokens(part)
+            assert pool.workspace_bytes(s.num_q_heads) <= ws.numel()
+            out.fill_(float("nan"))
+            pool.decode(dev.q[:nb], out[:nb], ws, scale=float(inp.scale))
+            torch.cuda.synchronize()
+            got = out[:nb].cpu().numpy()
+            assert max_err(got, want[:nb]) <= TOL["bf16"], (it, part, nb)
+    finally:
+        pool.close()
