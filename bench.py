@@ -1,21 +1,22 @@
 #!/usr/bin/env python3
 """Decode-attention bandwidth benchmark on one MI355X.
 
-One step = one decode-attention call (partition kernel + merge kernel) for
-one layer of the Llama-3-8B-shaped workload: batch 32, 32 query / 8 KV heads,
-head_dim 128, every context 4096 tokens, bf16 KV in 16-token blocks placed by
-a seeded random permutation of an 8192-block pool.  Inputs are synthetic and
+One step = one decode-attention call (one kernel launch) for one layer of
+the Llama-3-8B-shaped workload: batch 32, 32 query / 8 KV heads, head_dim
+128, every context 4096 tokens, bf16 KV in 16-token blocks placed by a
+seeded random permutation of an 8192-block pool.  Inputs are synthetic and
 resident in HBM before timing starts.  The timed loop cycles over
 ``--layers`` independent copies of the KV pool (different layers' caches),
 so no step finds its 512 MiB of KV in the 256 MB Infinity Cache that the
-previous step filled.
+previous steps filled.
 
 Printed: one JSON line on stdout.  ``value`` is KV bytes read per step
 (unique cached tokens x KV heads x head_dim x 2 (K and V) x element bytes)
 over the wall-clock time per step of the K timed steps.  ``roofline`` prices
-the partition kernel alone (HIP events around every launch in the timed
-loop) against MI355X's 8 TB/s HBM peak.  ``cpu_baseline`` times the float64
-CPU oracle on a bounded sample of the same workload.
+the attention kernel alone (HIP events around the launches of every
+``--layers``-th step of the timed loop) against MI355X's 8 TB/s HBM peak.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the
+same workload.
 """
 
 import argparse
@@ -32,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention KV-read TB/s, % of 8 TB/s HBM peak; µs per decode step"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_398_amd", "csrc", "pa_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partition_kernel_llama3_8b_b32_ctx4k.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_kernel_llama3_8b_b32_ctx4k.json")
 
 
 def log(msg):
@@ -109,7 +110,7 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_b32_ctx4k")
     ap.add_argument("--layers", type=int, default=8,
                     help="independent KV pools cycled by the timed loop")
-    ap.add_argument("--partition-tokens", type=int, default=0, help="0: automatic")
+    ap.add_argument("--workgroups", type=int, default=0, help="0: automatic")
     ap.add_argument("--heads-per-workgroup", type=int, default=0, help="0: automatic")
     ap.add_argument("--cold-iters", type=int, default=30,
                     help="extra steps timed after a 1 GiB cache flush each")
@@ -146,12 +147,12 @@ def main():
         vs = None if dev.v_scale is None else (dev.v_scale if r == 0 else dev.v_scale.clone())
         p = pa.PagedKVPool(k, v, s.kv_dtype, ks, vs)
         p.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
-        if args.partition_tokens:
-            p.set_partition_tokens(args.partition_tokens)
+        if args.workgroups:
+            p.set_workgroups(args.workgroups)
         if args.heads_per_workgroup:
             p.set_heads_per_workgroup(args.heads_per_workgroup)
         pools.append(p)
-    part_tokens = pools[0].partition_tokens()
+    nwg = pools[0].workgroups()
     hc = pools[0].heads_per_workgroup()
     ws_bytes = pools[0].workspace_bytes(s.num_q_heads)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
@@ -169,15 +170,15 @@ def main():
     # add several microseconds between back-to-back launches.
     n_prof = (args.steps + R - 1) // R
     pa.pa_profile_enable(pools[0].handle, n_prof)
-    log(f"timing {args.steps} steps (partition {part_tokens} tokens, {hc} KV heads per "
-        f"workgroup, {R} layers cycled, events on every {R}-th step)")
+    log(f"timing {args.steps} steps ({nwg} workgroups, {hc} KV heads per workgroup, "
+        f"{R} layers cycled, events on every {R}-th step)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    part_ms, merge_ms = pa.pa_profile_read(pools[0].handle, n_prof)
+    kern_ms = pa.pa_profile_read(pools[0].handle, n_prof)
     pa.pa_profile_enable(pools[0].handle, 0)
     if not bool(torch.isfinite(out).all()):
         raise RuntimeError("non-finite output")
@@ -185,11 +186,10 @@ def main():
     nbytes = kv_bytes(inp)
     sec_per_step = (t1 - t0) / args.steps
     tbs = nbytes / sec_per_step / 1e12
-    part_avg = statistics.fmean(part_ms) * 1e-3
-    merge_avg = statistics.fmean(merge_ms) * 1e-3
-    achieved = nbytes / part_avg / 1e9
-    log(f"{sec_per_step * 1e6:.1f} us/step, {tbs:.3f} TB/s; partition kernel "
-        f"{part_avg * 1e6:.1f} us ({achieved:.0f} GB/s), merge {merge_avg * 1e6:.1f} us")
+    kern_avg = statistics.fmean(kern_ms) * 1e-3
+    achieved = nbytes / kern_avg / 1e9
+    log(f"{sec_per_step * 1e6:.1f} us/step, {tbs:.3f} TB/s; attention kernel "
+        f"{kern_avg * 1e6:.1f} us ({achieved:.0f} GB/s) over {len(kern_ms)} event pairs")
 
     # cold steps: every step after reading 1 GiB elsewhere, which evicts the
     # KV from the caches without leaving dirty lines behind (flush outside
@@ -240,15 +240,14 @@ def main():
             "kv_heads": s.num_kv_heads, "head_dim": s.head_dim,
             "context_tokens": int(inp.max_context_len), "block_size": 16,
             "kv_dtype": s.kv_dtype, "q_dtype": s.q_dtype, "out_dtype": "f32",
-            "kv_bytes_per_step": nbytes, "partition_tokens": part_tokens,
+            "kv_bytes_per_step": nbytes, "workgroups": nwg,
             "layers_cycled": R, "kv_heads_per_workgroup": hc,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "partition_kernel", "kernel_us": round(part_avg * 1e6, 2),
-            "merge_us": round(merge_avg * 1e6, 2) if ws_bytes else None,
+            "kernel": "attention_kernel", "kernel_us": round(kern_avg * 1e6, 2),
         },
         "us_per_step": round(sec_per_step * 1e6, 2),
         "pct_of_hbm_peak": round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2),

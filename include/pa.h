@@ -29,8 +29,12 @@
  *
  * Conventions shared by every call.
  *   - Pointers named "device" point to GPU memory of the current HIP device;
- *     the caller allocates, owns and frees all of them.  The library never
- *     allocates or frees device memory; it owns only the host-side handle.
+ *     the caller allocates, owns and frees all of them.  The library owns
+ *     the host-side handle and one small device array per handle: arrival
+ *     counters (4 bytes per sequence and head chunk), allocated and cleared
+ *     on the first run that needs them (hipMalloc, so that first run waits
+ *     for the device), grown when the batch grows, freed by
+ *     pa_kv_pool_destroy.  Every run leaves them zero.
  *   - Work is enqueued asynchronously on the caller's stream (a hipStream_t
  *     passed as void*; NULL is the default stream).  No call synchronises,
  *     except pa_block_table_validate.  Device buffers must stay valid until
@@ -43,7 +47,9 @@
  *     give undefined *values* in out, never an out-of-bounds access: the
  *     kernels clamp lengths to max_context_len and skip block ids outside
  *     [0, num_blocks).
- *   - A handle is not thread-safe; distinct handles are independent.
+ *   - A handle is not thread-safe, and runs on one handle must be ordered
+ *     (one stream, or synchronised): they share its counters.  Distinct
+ *     handles are independent.
  */
 #ifndef PA_H
 #define PA_H
@@ -138,12 +144,15 @@ pa_status pa_block_table_validate(pa_kv_pool *pool, void *stream);
 /*
  * pa_decode_workspace_bytes -- device scratch a decode run needs.
  *
- * The context of each sequence is split into partitions processed in
- * parallel; each writes a running max, a running sum and an unnormalised
- * output per query head, later combined exactly by a log-sum-exp merge.
- * The size depends on the table set last (batch, max_context_len), the
- * partition length in force and num_q_heads.  *bytes receives the size
- * (0 when nothing needs storing).
+ * The kernel's workgroups take equal shares of the batch's 16-token blocks
+ * (whatever the mix of context lengths), so a sequence may be split
+ * between two or more workgroups.  Each piece of a split sequence leaves a
+ * running max, a running sum and an unnormalised output per query head,
+ * combined exactly (log-sum-exp) by the workgroup that finishes last.  The
+ * workspace holds two such records per workgroup; its size depends on the
+ * workgroup count and head chunk in force (pa_decode_workgroups,
+ * pa_decode_heads_per_workgroup) and on num_q_heads, not on the lengths.
+ * *bytes receives the size (0 with a single workgroup).
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_SHAPE.
  */
 pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads,
@@ -160,7 +169,7 @@ pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads,
  * out: device float32 [batch][num_q_heads][head_dim], written in full.
  * workspace: device, 256-byte aligned, at least pa_decode_workspace_bytes;
  *   its contents are scratch (no need to clear).  May be NULL when that
- *   size is 0.
+ *   size is 0.  Runs that overlap in time must not share a workspace.
  * stream: hipStream_t of the caller.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE (pool is FP8, or q_dtype
  *   does not match), PA_ERR_UNSUPPORTED (group size), PA_ERR_STATE (no
@@ -185,27 +194,23 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
                             size_t workspace_bytes, void *stream);
 
 /*
- * pa_decode_set_partition_tokens -- override the context partition length.
+ * pa_decode_set_workgroups -- override the number of workgroups.
  *
- * tokens: 0 restores the automatic choice; otherwise a multiple of 16 in
- * [16, 1 << 20].  Any value gives the same result up to rounding (the
- * merge is exact); it only changes parallelism and workspace size.
- * Automatic choice: the whole context (one partition, no merge, no
- * workspace) when batch * num_kv_heads / heads_per_workgroup >= 256;
- * otherwise the longest context is cut into ceil(256 / that product)
- * partitions.  The choice sees only max_context_len: for batches of very
- * uneven lengths a caller that knows them may do better with a shorter
- * partition (the grid then balances itself over the compute units).
+ * count: 0 restores the automatic choice (one per compute unit, 256, or
+ * fewer when the batch has fewer 16-token blocks per head chunk);
+ * otherwise 1 .. 65536.  Any value gives the same result up to rounding
+ * (the merge of split sequences is exact); it only changes parallelism and
+ * the workspace size.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
  */
-pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens);
+pa_status pa_decode_set_workgroups(pa_kv_pool *pool, int32_t count);
 
 /*
- * pa_decode_partition_tokens -- partition length the next run will use for
- * the table set last (after the automatic choice or an override).
+ * pa_decode_workgroups -- workgroup count the next run will use for the
+ * table set last (after the automatic choice or an override).
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set).
  */
-pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens);
+pa_status pa_decode_workgroups(const pa_kv_pool *pool, int32_t *count);
 
 /*
  * pa_decode_set_heads_per_workgroup -- override how many adjacent KV heads
@@ -216,7 +221,8 @@ pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens);
  * value gives the same result; it changes how many contiguous bytes of
  * each block one workgroup reads and how many workgroups there are.
  * Automatic choice: the largest chunk for which batch * num_kv_heads /
- * heads still gives each of the 256 compute units a workgroup, else 1.
+ * heads is still at least 256 (with equal context lengths, each
+ * workgroup's share is then whole sequences), else the largest allowed.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
  */
 pa_status pa_decode_set_heads_per_workgroup(pa_kv_pool *pool, int32_t heads);
@@ -232,9 +238,9 @@ pa_status pa_decode_heads_per_workgroup(const pa_kv_pool *pool, int32_t *heads);
  * pa_profile_enable -- time the attention kernel of the next runs.
  *
  * While enabled (capacity > 0), each run records a pair of HIP events on
- * its stream around its partition kernel and another around its merge
- * kernel, for up to `capacity` runs; capacity 0 disables and releases the
- * events.  Events are host-side HIP objects, not device memory.
+ * its stream around its kernel, for up to `capacity` runs; capacity 0
+ * disables and releases the events.  Events are host-side HIP objects, not
+ * device memory.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE (capacity < 0), PA_ERR_HIP.
  */
 pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity);
@@ -243,12 +249,12 @@ pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity);
  * pa_profile_read -- per-run kernel durations recorded since enabling.
  *
  * Waits for the recorded events, writes up to `capacity` durations in
- * milliseconds to partition_ms[i] and merge_ms[i] (either may be NULL) and
- * the number of recorded runs to *count, then starts a new recording.
+ * milliseconds to kernel_ms[i] (may be NULL) and the number of recorded
+ * runs to *count, then starts a new recording.
  * Errors: PA_ERR_NULL, PA_ERR_STATE (profiling not enabled), PA_ERR_HIP.
  */
-pa_status pa_profile_read(pa_kv_pool *pool, float *partition_ms, float *merge_ms,
-                          int32_t capacity, int32_t *count);
+pa_status pa_profile_read(pa_kv_pool *pool, float *kernel_ms, int32_t capacity,
+                          int32_t *count);
 
 /* Static text for a status code. */
 const char *pa_status_str(pa_status status);

@@ -16,10 +16,10 @@ from .binding import (  # noqa: F401
     pa_block_table_validate,
     pa_decode_fp8_run,
     pa_decode_heads_per_workgroup,
-    pa_decode_partition_tokens,
     pa_decode_run,
     pa_decode_set_heads_per_workgroup,
-    pa_decode_set_partition_tokens,
+    pa_decode_set_workgroups,
+    pa_decode_workgroups,
     pa_decode_workspace_bytes,
     pa_kv_pool_create,
     pa_kv_pool_destroy,
@@ -55,11 +55,11 @@ class PagedKVPool:
         self.batch = b
         pa_block_table_set(self.handle, block_table, context_lens, b, mb, max_context_len)
 
-    def set_partition_tokens(self, tokens):
-        pa_decode_set_partition_tokens(self.handle, tokens)
+    def set_workgroups(self, count):
+        pa_decode_set_workgroups(self.handle, count)
 
-    def partition_tokens(self):
-        return pa_decode_partition_tokens(self.handle)
+    def workgroups(self):
+        return pa_decode_workgroups(self.handle)
 
     def set_heads_per_workgroup(self, heads):
         pa_decode_set_heads_per_workgroup(self.handle, heads)

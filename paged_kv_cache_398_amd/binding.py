@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Optional
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
 
@@ -32,13 +32,12 @@ SIGNATURES = [
     ("pa_decode_workspace_bytes", _i32, [_vp, _i32, ctypes.POINTER(_sz)]),
     ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
-    ("pa_decode_set_partition_tokens", _i32, [_vp, _i32]),
-    ("pa_decode_partition_tokens", _i32, [_vp, ctypes.POINTER(_i32)]),
+    ("pa_decode_set_workgroups", _i32, [_vp, _i32]),
+    ("pa_decode_workgroups", _i32, [_vp, ctypes.POINTER(_i32)]),
     ("pa_decode_set_heads_per_workgroup", _i32, [_vp, _i32]),
     ("pa_decode_heads_per_workgroup", _i32, [_vp, ctypes.POINTER(_i32)]),
     ("pa_profile_enable", _i32, [_vp, _i32]),
-    ("pa_profile_read", _i32, [_vp, ctypes.POINTER(_f32), ctypes.POINTER(_f32), _i32,
-                               ctypes.POINTER(_i32)]),
+    ("pa_profile_read", _i32, [_vp, ctypes.POINTER(_f32), _i32, ctypes.POINTER(_i32)]),
     ("pa_status_str", ctypes.c_char_p, [_i32]),
     ("pa_last_error", ctypes.c_char_p, []),
 ]
@@ -148,13 +147,13 @@ def pa_decode_fp8_run(pool, q, q_dtype, num_q_heads, scale, out, workspace, work
                                             workspace_bytes, _stream(stream)))
 
 
-def pa_decode_set_partition_tokens(pool, tokens) -> None:
-    _check(load_library().pa_decode_set_partition_tokens(pool, tokens))
+def pa_decode_set_workgroups(pool, count) -> None:
+    _check(load_library().pa_decode_set_workgroups(pool, count))
 
 
-def pa_decode_partition_tokens(pool) -> int:
+def pa_decode_workgroups(pool) -> int:
     t = _i32()
-    _check(load_library().pa_decode_partition_tokens(pool, ctypes.byref(t)))
+    _check(load_library().pa_decode_workgroups(pool, ctypes.byref(t)))
     return t.value
 
 
@@ -172,13 +171,12 @@ def pa_profile_enable(pool, capacity) -> None:
     _check(load_library().pa_profile_enable(pool, capacity))
 
 
-def pa_profile_read(pool, capacity) -> Tuple[list, list]:
-    part = (_f32 * max(capacity, 1))()
-    merge = (_f32 * max(capacity, 1))()
+def pa_profile_read(pool, capacity) -> list:
+    """Kernel durations (ms) of the runs recorded since enabling."""
+    kern = (_f32 * max(capacity, 1))()
     n = _i32()
-    _check(load_library().pa_profile_read(pool, part, merge, capacity, ctypes.byref(n)))
-    k = min(n.value, capacity)
-    return list(part[:k]), list(merge[:k])
+    _check(load_library().pa_profile_read(pool, kern, capacity, ctypes.byref(n)))
+    return list(kern[:min(n.value, capacity)])
 
 
 def pa_status_str(status) -> str:

@@ -1,9 +1,10 @@
-// pa_api.cpp -- the C ABI of include/pa.h: argument validation, partition
+// pa_api.cpp -- the C ABI of include/pa.h: argument validation, launch
 // choice, workspace layout and kernel launches on the caller's stream.
 //
 // Every entry point validates on the host before touching the HIP runtime,
-// so argument errors are reported without a GPU.  The library allocates no
-// device memory; callers pass every buffer.
+// so argument errors are reported without a GPU.  Callers pass every data
+// buffer; the only device memory the library allocates is a handle's small
+// array of arrival counters (4 bytes per sequence and head chunk).
 
 #include <hip/hip_runtime.h>
 
@@ -26,11 +27,14 @@ struct pa_kv_pool {
   bool table_set = false;
   const int32_t *block_table = nullptr, *context_lens = nullptr;
   int32_t batch = 0, max_blocks_per_seq = 0, max_context_len = 0;
-  int32_t partition_override = 0;  // 0: automatic
-  int32_t heads_override = 0;      // 0: automatic
+  int32_t workgroups_override = 0;  // 0: automatic
+  int32_t heads_override = 0;       // 0: automatic
+  // arrival counters of split (sequence, chunk) pairs: device, zero between runs
+  uint32_t *counters = nullptr;
+  size_t counter_capacity = 0;  // in counters
   // profiling
   int32_t prof_capacity = 0, prof_count = 0;
-  std::vector<hipEvent_t> prof_events;  // 3 per run: before, between, after
+  std::vector<hipEvent_t> prof_events;  // 2 per run: before and after the kernel
 };
 
 namespace {
@@ -65,8 +69,8 @@ int kind_of(pa_dtype t) {
 // MI355X: 256 compute units in 8 XCDs.  The launch shape (and so the
 // workspace size) depends only on the arguments, never on a runtime query.
 constexpr int64_t kComputeUnits = 256;
-// Longest partition (tokens); keeps every token index of the kernels in int32.
-constexpr int32_t kMaxPartition = 1 << 20;
+// Most workgroups a caller may ask for.
+constexpr int32_t kMaxWorkgroups = 1 << 16;
 
 // Largest head chunk a workgroup may take: a power of two dividing both
 // num_kv_heads and kWaves (each wave works on one head of the chunk).
@@ -76,11 +80,19 @@ int32_t max_heads_per_workgroup(int32_t hkv) {
   return hc;
 }
 
-// KV heads per workgroup.  Automatic choice: the largest chunk that still
-// gives every compute unit a (sequence, chunk) of its own, so that contexts
-// need not be split (no partial results, no merge); wider chunks read
-// longer contiguous runs of each block.  When even single heads are too few
-// the contexts must be split anyway, and then the widest chunk is best.
+// Upper bound of the work units (16-token blocks of one (sequence, head
+// chunk)) for head chunk hc, from the host-side bound of the lengths.
+int64_t max_units(const pa_kv_pool *p, int32_t hc) {
+  const int64_t blocks = (p->max_context_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+  return (int64_t)p->batch * (p->num_kv_heads / hc) * blocks;
+}
+
+// KV heads per workgroup.  Automatic choice: the largest chunk for which the
+// (sequence, chunk) pairs still number at least one per compute unit, so
+// that when the contexts are of equal length every workgroup's range is one
+// whole pair (no partial results); wider chunks read longer contiguous runs
+// of each block.  When even single heads are too few, pairs are split
+// anyway, and then the widest chunk is best.
 int32_t heads_per_workgroup(const pa_kv_pool *p) {
   if (p->heads_override > 0) return p->heads_override;
   const int32_t hmax = max_heads_per_workgroup(p->num_kv_heads);
@@ -89,38 +101,28 @@ int32_t heads_per_workgroup(const pa_kv_pool *p) {
   return hmax;
 }
 
-// Tokens per context partition (a multiple of 16).  Automatic choice: the
-// whole context when the (sequence, chunk) pairs already cover the compute
-// units (no partial results, no merge); otherwise the context is cut into
-// as many partitions as it takes to give each compute unit a workgroup.
-int32_t partition_tokens(const pa_kv_pool *p) {
-  if (p->partition_override > 0) return p->partition_override;
-  const int64_t units = (int64_t)p->batch * (p->num_kv_heads / heads_per_workgroup(p));
-  const int64_t parts = units >= kComputeUnits ? 1 : (kComputeUnits + units - 1) / std::max<int64_t>(units, 1);
-  // whole context: rounded up to a block; split: rounded down, so that the
-  // split gives at least `parts` partitions
-  const int64_t ctx = p->max_context_len;
-  const int64_t tokens = parts == 1 ? (ctx + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE * PA_BLOCK_SIZE
-                                    : ctx / parts / PA_BLOCK_SIZE * PA_BLOCK_SIZE;
-  return (int32_t)std::min<int64_t>(std::max<int64_t>(tokens, PA_BLOCK_SIZE), kMaxPartition);
+// Workgroups: one per compute unit (fewer if there are fewer units of work).
+int32_t workgroups(const pa_kv_pool *p) {
+  if (p->workgroups_override > 0) return p->workgroups_override;
+  const int64_t u = max_units(p, heads_per_workgroup(p));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(kComputeUnits, u));
 }
 
 struct Layout {
-  int32_t part_tokens, parts, hc, chunks;
+  int32_t nwg, hc, chunks;
   size_t ml_bytes, acc_offset, total;
 };
 
+// Workspace: two partial records per workgroup (the pieces its range starts
+// and ends with), each hc * G query heads of (max, sum) and d floats.
 Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
   Layout L{};
-  L.part_tokens = partition_tokens(p);
-  // at least one partition: its workgroups also write the zero rows of
-  // empty sequences
-  L.parts = (int32_t)std::max<int64_t>(
-      1, (p->max_context_len + (int64_t)L.part_tokens - 1) / L.part_tokens);
   L.hc = heads_per_workgroup(p);
   L.chunks = p->num_kv_heads / L.hc;
-  // a single partition writes the output directly; no partials to keep
-  const size_t recs = L.parts > 1 ? (size_t)p->batch * hq * L.parts : 0;
+  L.nwg = workgroups(p);
+  const int32_t hcg = L.hc * (hq / p->num_kv_heads);
+  // one workgroup never splits a (sequence, chunk): no partials to keep
+  const size_t recs = L.nwg > 1 ? (size_t)L.nwg * 2 * hcg : 0;
   L.ml_bytes = recs * sizeof(float2);
   L.acc_offset = (L.ml_bytes + 255) & ~(size_t)255;
   L.total = recs ? L.acc_offset + recs * p->head_dim * sizeof(float) : 0;
@@ -156,14 +158,35 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
     if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   }
-  const size_t wgs = (size_t)pool->batch * L.chunks * L.parts;
-  if (wgs * pa::kWaves * 64 >= (size_t(1) << 32) || (size_t)pool->batch * hq >= (size_t(1) << 31))
-    return fail(PA_ERR_SHAPE, "launch grid too large (raise the partition length)");
+  if ((size_t)pool->batch * hq >= (size_t(1) << 31))
+    return fail(PA_ERR_SHAPE, "batch * num_q_heads too large");
   if (pool->batch == 0) return ok();
 
   // ---- from here on HIP is used
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  // Arrival counters of split (sequence, chunk) pairs: owned by the handle,
+  // zero between runs (the merging workgroup resets its counter).  Grown,
+  // and cleared by a kernel, only when the batch needs more of them.
+  const size_t ncnt = (size_t)pool->batch * L.chunks;
+  if (ncnt > pool->counter_capacity) {
+    // hipFree waits for the device, so no run still uses the old counters
+    if (pool->counters && (e = hipFree(pool->counters)) != hipSuccess)
+      return fail(PA_ERR_HIP, "hipFree(counters): %s", hipGetErrorString(e));
+    pool->counters = nullptr;
+    pool->counter_capacity = 0;
+    const size_t cap = std::max<size_t>(ncnt, 1024);
+    void *ptr = nullptr;
+    if ((e = hipMalloc(&ptr, cap * sizeof(uint32_t))) != hipSuccess)
+      return fail(PA_ERR_HIP, "hipMalloc(counters): %s", hipGetErrorString(e));
+    if ((e = pa::launch_zero(static_cast<uint32_t *>(ptr), cap, s)) != hipSuccess) {
+      (void)hipFree(ptr);
+      return fail(PA_ERR_HIP, "clearing the counters: %s", hipGetErrorString(e));
+    }
+    pool->counters = static_cast<uint32_t *>(ptr);
+    pool->counter_capacity = cap;
+  }
+
   pa::LaunchArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
@@ -175,6 +198,7 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   a.out = out;
   a.ws_ml = static_cast<float2 *>(workspace);
   a.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.acc_offset);
+  a.counters = pool->counters;
   a.num_blocks = pool->num_blocks;
   a.hkv = pool->num_kv_heads;
   a.hq = hq;
@@ -182,25 +206,20 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   a.batch = pool->batch;
   a.max_blocks = pool->max_blocks_per_seq;
   a.max_ctx = pool->max_context_len;
-  a.part_tokens = L.part_tokens;
-  a.parts = L.parts;
+  a.nwg = L.nwg;
   a.hc = L.hc;
   a.chunks = L.chunks;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.kv = kind_of(pool->kv_dtype);
 
   const bool prof = pool->prof_capacity > 0 && pool->prof_count < pool->prof_capacity;
-  hipEvent_t *ev = prof ? &pool->prof_events[3 * (size_t)pool->prof_count] : nullptr;
+  hipEvent_t *ev = prof ? &pool->prof_events[2 * (size_t)pool->prof_count] : nullptr;
   if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess)
     return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = pa::launch_partition(a, s)) != hipSuccess)
-    return fail(PA_ERR_HIP, "partition kernel launch: %s", hipGetErrorString(e));
-  if (prof && (e = hipEventRecord(ev[1], s)) != hipSuccess)
-    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = pa::launch_merge(a, s)) != hipSuccess)
-    return fail(PA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  if ((e = pa::launch_attention(a, s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
   if (prof) {
-    if ((e = hipEventRecord(ev[2], s)) != hipSuccess)
+    if ((e = hipEventRecord(ev[1], s)) != hipSuccess)
       return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
     ++pool->prof_count;
   }
@@ -261,6 +280,7 @@ pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_
 void pa_kv_pool_destroy(pa_kv_pool *pool) {
   if (!pool) return;
   release_events(pool);
+  if (pool->counters) (void)hipFree(pool->counters);
   delete pool;
 }
 
@@ -335,18 +355,18 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
   return run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes, stream, true);
 }
 
-pa_status pa_decode_set_partition_tokens(pa_kv_pool *pool, int32_t tokens) {
+pa_status pa_decode_set_workgroups(pa_kv_pool *pool, int32_t count) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
-  if (tokens != 0 && (tokens < PA_BLOCK_SIZE || tokens % PA_BLOCK_SIZE || tokens > kMaxPartition))
-    return fail(PA_ERR_SHAPE, "partition length %d: 0 or a multiple of 16 in [16, 2^20]", tokens);
-  pool->partition_override = tokens;
+  if (count < 0 || count > kMaxWorkgroups)
+    return fail(PA_ERR_SHAPE, "workgroups %d: 0 or in [1, %d]", count, kMaxWorkgroups);
+  pool->workgroups_override = count;
   return ok();
 }
 
-pa_status pa_decode_partition_tokens(const pa_kv_pool *pool, int32_t *tokens) {
-  if (!pool || !tokens) return fail(PA_ERR_NULL, "pool or tokens is NULL");
+pa_status pa_decode_workgroups(const pa_kv_pool *pool, int32_t *count) {
+  if (!pool || !count) return fail(PA_ERR_NULL, "pool or count is NULL");
   if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set");
-  *tokens = partition_tokens(pool);
+  *count = workgroups(pool);
   return ok();
 }
 
@@ -372,7 +392,7 @@ pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity) {
   if (capacity < 0) return fail(PA_ERR_SHAPE, "capacity %d < 0", capacity);
   release_events(pool);
   if (capacity == 0) return ok();
-  pool->prof_events.resize(3 * (size_t)capacity);
+  pool->prof_events.resize(2 * (size_t)capacity);
   for (auto &e : pool->prof_events) {
     hipError_t r = hipEventCreate(&e);
     if (r != hipSuccess) {
@@ -385,24 +405,21 @@ pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity) {
   return ok();
 }
 
-pa_status pa_profile_read(pa_kv_pool *pool, float *partition_ms, float *merge_ms,
-                          int32_t capacity, int32_t *count) {
+pa_status pa_profile_read(pa_kv_pool *pool, float *kernel_ms, int32_t capacity, int32_t *count) {
   if (!pool || !count) return fail(PA_ERR_NULL, "pool or count is NULL");
   if (pool->prof_capacity == 0) return fail(PA_ERR_STATE, "profiling not enabled");
   const int32_t n = pool->prof_count;
   *count = n;
   if (n > 0) {
-    hipError_t e = hipEventSynchronize(pool->prof_events[3 * (size_t)n - 1]);
+    hipError_t e = hipEventSynchronize(pool->prof_events[2 * (size_t)n - 1]);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
   }
   for (int32_t i = 0; i < n && i < capacity; ++i) {
-    hipEvent_t *ev = &pool->prof_events[3 * (size_t)i];
-    float t0 = 0.f, t1 = 0.f;
-    hipError_t e = hipEventElapsedTime(&t0, ev[0], ev[1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&t1, ev[1], ev[2]);
+    float t = 0.f;
+    hipError_t e = hipEventElapsedTime(&t, pool->prof_events[2 * (size_t)i],
+                                       pool->prof_events[2 * (size_t)i + 1]);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
-    if (partition_ms) partition_ms[i] = t0;
-    if (merge_ms) merge_ms[i] = t1;
+    if (kernel_ms) kernel_ms[i] = t;
   }
   pool->prof_count = 0;
   return ok();

@@ -30,11 +30,11 @@ struct LaunchArgs {
   const int32_t *table;     // [batch][max_blocks]
   const int32_t *ctx;       // [batch]
   float *out;               // [batch][hq][d]
-  float2 *ws_ml;            // [batch][hq][parts] (running max, running sum)
-  float *ws_acc;            // [batch][hq][parts][d] unnormalised output
+  float2 *ws_ml;            // [nwg][2][hc*G] partial (running max, running sum)
+  float *ws_acc;            // [nwg][2][hc*G][d] partial unnormalised output
+  uint32_t *counters;       // [batch][chunks] arrival counters, zero between runs
   int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx;
-  int32_t part_tokens;      // tokens per partition (multiple of 16)
-  int32_t parts;            // ceil(max_ctx / part_tokens)
+  int32_t nwg;              // workgroups (equal ranges of the work)
   int32_t hc;               // KV heads per workgroup (divides hkv and kWaves)
   int32_t chunks;           // hkv / hc
   float scale_log2e;        // softmax scale * log2(e)
@@ -44,11 +44,11 @@ struct LaunchArgs {
 // True when a kernel is built for (kv, head_dim, group size).
 bool kernel_supported(int kv, int d, int group);
 
-// Enqueue the attention kernel (grid batch * chunks * parts workgroups).
-hipError_t launch_partition(const LaunchArgs &a, hipStream_t stream);
+// Enqueue the attention kernel (grid nwg workgroups of kWaves waves).
+hipError_t launch_attention(const LaunchArgs &a, hipStream_t stream);
 
-// Enqueue the log-sum-exp merge kernel (grid batch * hq workgroups); a no-op
-// when there is a single partition (the attention kernel then writes out).
-hipError_t launch_merge(const LaunchArgs &a, hipStream_t stream);
+// Enqueue a kernel that sets n 32-bit words to zero (a kernel rather than a
+// memset, so that a captured graph replays it faithfully).
+hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t stream);
 
 }  // namespace pa

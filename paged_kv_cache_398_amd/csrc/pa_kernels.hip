@@ -8,34 +8,34 @@
 // 与三路省内存方案", sections 一, 三 and 六; grouping of query heads as in the
 // GQA section of "大模型推理为何这么慢？从内存带宽瓶颈到KV Cache优化的技术突围").
 //
-// How:
+// How (one kernel, attention_kernel; details above it):
 //
-// 1. partition_kernel: one workgroup of kWaves waves per (sequence, chunk of
-//    hc adjacent KV heads, context partition).  Wave w works on head
-//    w % hc of the chunk and takes every (kWaves/hc)-th 16-token block of the
-//    partition, so the workgroup as a whole reads the hc heads' rows of
-//    every block it touches: hc * head_dim * elem bytes contiguous per token.
-//    A wave holds a whole block of its head in registers: each token row is
-//    split over LPT lanes, 64/LPT tokens per pass, with 8- or 16-byte loads
-//    per lane.  Every K/V element is loaded from HBM once and used by all G
-//    query heads of its group, which sit in the same lane's registers.  The
-//    loop is a two-stage software pipeline: the next block's loads are in
-//    flight while the current block is computed, and the block table of up
-//    to 64 blocks is read by one vector load before it starts.
-//    Scores are reduced over the LPT lanes of a token with DPP.  The
+//  - The work is counted in units (one 16-token block of one (sequence,
+//    chunk of hc adjacent KV heads) pair) and split into equal contiguous
+//    ranges, one per workgroup of kWaves waves, whatever the mix of context
+//    lengths.  A range is cut into pieces at pair boundaries.
+//  - In a piece, wave w works on head w % hc of the chunk and takes every
+//    (kWaves/hc)-th block.  A wave holds a whole block of its head in
+//    registers: each token row is split over LPT lanes, 64/LPT tokens per
+//    pass, with 8- or 16-byte loads per lane.  Every K/V element is loaded
+//    from HBM once and used by all G query heads of its group, which sit in
+//    the same lane's registers.  The loop is a two-stage software pipeline:
+//    the next block's loads are in flight while the current block is
+//    computed, and the block table of up to 64 blocks is read by one vector
+//    load before it starts.
+//  - Scores are reduced over the LPT lanes of a token with DPP.  The
 //    softmax is accumulated online (running max and sum, as in the
 //    FlashAttention sections of the pages): the running max is kept
 //    wave-uniform and is only raised when a block's maximum exceeds it by
 //    more than kTau (log2 units), so the rescale of the accumulators is
 //    rare; any running max gives the same normalised result, it only bounds
-//    the exponentials (by 2^kTau).  At the end the lanes' states and the
-//    phases of each head are combined exactly in LDS.  With one partition
-//    the normalised output is written directly; otherwise (max, sum,
-//    unnormalised output) per query head and partition.
-//
-// 2. merge_kernel (only with several partitions): one workgroup per
-//    (sequence, query head) combines the partitions: M = max_p m_p,
-//    w_p = 2^(m_p - M), out = sum w_p acc_p / sum w_p l_p.
+//    the exponentials (by 2^kTau).
+//  - At the end of a piece the lanes' states and the phases of each head
+//    are combined exactly in LDS.  A piece that is a whole pair writes the
+//    normalised output; a pair split between ranges leaves a (max, sum,
+//    unnormalised output) record per piece, and the last piece to finish
+//    merges them (log-sum-exp: M = max_p m_p, w_p = 2^(m_p - M),
+//    out = sum w_p acc_p / sum w_p l_p).
 //
 // Positions past a sequence's length contribute exactly nothing (selects,
 // not multiplications, so NaN garbage in unused slots cannot leak), table
@@ -177,47 +177,24 @@ struct Block {  // one block's K/V slice held by one lane
   bool ok;                            // block id in range
 };
 
+// The query rows of the G heads of KV head g, sliced as the lanes of a wave
+// hold K/V: lane-local fp32 copies, and bf16 pairs for the bf16 dot product.
 template <int KV, int D, int G>
-__global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
+struct Query {
   using C = Cfg<KV, D, G>;
-  constexpr int LPT = C::LPT, NPASS = C::NPASS, DW = C::DW, EPL = C::EPL;
+  float f[G][C::EPL];
+  uint32_t bf2[G][C::DW];
+};
+
+template <int KV, int D, int G>
+__device__ __forceinline__ void load_query(const LaunchArgs &a, int b, int g, Query<KV, D, G> &qry) {
+  using C = Cfg<KV, D, G>;
+  constexpr int LPT = C::LPT;
   const int lane = threadIdx.x & 63;
-  // wave index, known wave-uniform: everything derived from it stays scalar
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int sub = lane % LPT;   // which slice of the row
-  const int slot = lane / LPT;  // which token of the pass
-
-  // workgroup -> (sequence, head chunk, partition); partitions fastest
-  int u = blockIdx.x;
-  const int part = u % a.parts;
-  u /= a.parts;
-  const int chunk = u % a.chunks;
-  const int b = u / a.chunks;
-  // wave -> (KV head of the chunk, phase); the phases of a head split its blocks
-  const int hc = a.hc;
-  const int nph = kWaves / hc;
-  const int hl = w % hc;
-  const int ph = w / hc;
-  const int g = chunk * hc + hl;
-  const int h0 = g * G;  // first query head of this wave's group
-
-  const int n = min(max(a.ctx[b], 0), a.max_ctx);
-  const int tok0 = part * a.part_tokens;
-  if (tok0 >= n) {  // whole workgroup: nothing of this sequence here
-    if (part == 0) {  // empty sequence: its output rows are zero
-      for (int idx = threadIdx.x; idx < hc * G * D; idx += kThreads)
-        a.out[((size_t)b * a.hq + chunk * hc * G) * D + idx] = 0.f;
-    }
-    return;
-  }
-  const int tok_end = min(n, tok0 + a.part_tokens);
-  const int blk0 = tok0 / kBlock;
-  const int nblk = (tok_end - tok0 + kBlock - 1) / kBlock;
-  const int nb_w = nblk > ph ? (nblk - ph + nph - 1) / nph : 0;
-
-  // ---- query slice of the G heads of this group (lane-local elements)
-  float qf[G][EPL];
-  uint32_t q2[G][DW];  // bf16 pairs (bf16 pools only)
+  const int sub = lane % LPT;
+  const int h0 = g * G;
+  float(&qf)[G][C::EPL] = qry.f;
+  uint32_t(&q2)[G][C::DW] = qry.bf2;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
@@ -242,14 +219,54 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
     }
   }
 
+}
+
+// Table entries of up to 64 of a wave's blocks, one per lane: lane j holds
+// the entry of the wave's block c0 + j (block blk0 + ph + (c0 + j) * nph of
+// the sequence), -1 past the wave's nb_w blocks.
+__device__ __forceinline__ int load_table(const LaunchArgs &a, int b, int blk0, int ph, int nph,
+                                          int c0, int nb_w) {
+  const int lane = threadIdx.x & 63;
+  const int *trow = a.table + (size_t)b * a.max_blocks + blk0 + ph;
+  return c0 + lane < nb_w ? trow[(size_t)(c0 + lane) * nph] : -1;
+}
+
+// Blocks of a piece that fall to the wave of phase ph.
+__device__ __forceinline__ int wave_blocks(int tok0, int tok_end, int ph, int nph) {
+  const int nblk = (tok_end - tok0 + kBlock - 1) / kBlock;
+  return nblk > ph ? (nblk - ph + nph - 1) / nph : 0;
+}
+
+// One wave's share of a piece: tokens [tok0, tok_end) of sequence b (tok0 a
+// multiple of 16), KV head g; the wave takes blocks ph, ph + nph, ... of the
+// piece.  qry holds the query rows (load_query) and tv0 the table entries of
+// the wave's first 64 blocks (load_table), both loaded by the caller so that
+// they can be in flight early.  Leaves the wave's exact state (running max,
+// sum, unnormalised output of each of the G query heads) in s_m[w], s_l[w],
+// s_acc[w].
+template <int KV, int D, int G>
+__device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, int tok0,
+                                             int tok_end, int ph, int nph, int w,
+                                             const Query<KV, D, G> &qry, int tv0,
+                                             float (*s_acc)[G][D], float (*s_m)[G],
+                                             float (*s_l)[G]) {
+  using C = Cfg<KV, D, G>;
+  constexpr int LPT = C::LPT, NPASS = C::NPASS, DW = C::DW, EPL = C::EPL;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % LPT;   // which slice of the row
+  const int slot = lane / LPT;  // which token of the pass
+  const int blk0 = tok0 / kBlock;
+  const int nb_w = wave_blocks(tok0, tok_end, ph, nph);
+
+  const float(&qf)[G][EPL] = qry.f;
+  const uint32_t(&q2)[G][DW] = qry.bf2;
+
   // ---- lane offsets inside a block, and the block table of this wave
   const size_t block_bytes = (size_t)kBlock * a.hkv * C::ROW;
   uint32_t lane_off[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p)
     lane_off[p] = (uint32_t)(((p * C::TPP + slot) * a.hkv + g) * C::ROW + sub * C::CH);
-  // i-th block of this wave: table entry trow[i * nph]
-  const int *trow = a.table + (size_t)b * a.max_blocks + blk0 + ph;
   const char *kbase = static_cast<const char *>(a.k_cache);
   const char *vbase = static_cast<const char *>(a.v_cache);
 
@@ -370,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
   // pipeline starts, so the loop itself reads nothing but K and V.
   for (int c0 = 0; c0 < nb_w; c0 += 64) {
     const int cn = min(64, nb_w - c0);
-    const int tv = c0 + lane < nb_w ? trow[(size_t)(c0 + lane) * nph] : -1;
+    const int tv = c0 == 0 ? tv0 : load_table(a, b, blk0, ph, nph, c0, nb_w);
     auto entry = [&](int i) { return __builtin_amdgcn_readlane(tv, min(i, cn - 1)); };
     Block<KV, D, G> A, B;
     issue(A, c0, entry(0));
@@ -403,8 +420,6 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[hh][e] = slot_reduce<LPT, false>(acc[hh][e]);
   }
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
   if (lane < LPT) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -421,139 +436,337 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(LaunchArgs a) {
       s_l[w][hh] = l[hh];
     }
   }
-  __syncthreads();
-  // outputs of this workgroup: hc heads x G query rows x D, query heads
-  // chunk*hc*G .. (chunk+1)*hc*G - 1 of sequence b
-  const size_t bh0 = (size_t)b * a.hq + (size_t)chunk * hc * G;
-  for (int idx = threadIdx.x; idx < hc * G * D; idx += kThreads) {
-    const int r = idx / D, e = idx % D;  // r = hl * G + hh
-    const int hh = r % G, hw = r / G;
-    float M = -__builtin_huge_valf();
-    for (int v = 0; v < nph; ++v) M = fmaxf(M, s_m[v * hc + hw][hh]);
-    float A = 0.f, L = 0.f;
-    for (int v = 0; v < nph; ++v) {
-      const int wv = v * hc + hw;
-      const float mv = s_m[wv][hh];
-      const float sc = mv == -__builtin_huge_valf() ? 0.f : fast_exp2(mv - M);
-      A = fmaf(sc, s_acc[wv][hh][e], A);
-      L = fmaf(sc, s_l[wv][hh], L);
-    }
-    if (a.parts == 1) {
-      a.out[(bh0 + r) * D + e] = L > 0.f ? A / L : 0.f;
-    } else {
-      const size_t rec = (bh0 + r) * a.parts + part;
-      a.ws_acc[rec * D + e] = A;
-      if (e == 0) a.ws_ml[rec] = make_float2(M, L);
-    }
-  }
 }
 
-// ---------------------------------------------------------------------------
-// merge kernel: one workgroup of kMergeThreads per (sequence, query head)
-//
-// M = max_p m_p; w_p = 2^(m_p - M) (0 for a partition that saw no valid
-// token); out = sum_p w_p acc_p / sum_p w_p l_p.  The partitions are spread
-// over the workgroup: thread t takes columns 4*(t % (D/4)) .. +3 of every
-// (kMergeThreads / (D/4))-th partition, with four partitions' loads in flight.
+// Exact combination of weighted partial states: the running maxima of the
+// parts are aligned to their common maximum M (a part that saw no valid
+// token has m = -inf and weight 0).
+__device__ __forceinline__ float part_weight(float m, float M) {
+  return m == -__builtin_huge_valf() ? 0.f : fast_exp2(m - M);
+}
 
-constexpr int kMergeThreads = 256;
-
-__device__ __forceinline__ float block_reduce(float x, float *scratch, bool is_max) {
-  // wave reduction (every lane ends with the result), then across waves
+// Sum over the workgroup (int64), every thread gets the result.
+__device__ __forceinline__ long long block_sum(long long x, long long *scratch) {
 #pragma unroll
-  for (int off = 32; off >= 1; off /= 2) {
-    const float y = __shfl_xor(x, off);
-    x = is_max ? fmaxf(x, y) : x + y;
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) scratch[w] = x;
+  for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off);
   __syncthreads();
-  float r = scratch[0];
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  long long r = 0;
 #pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
-  __syncthreads();
+  for (int i = 0; i < kWaves; ++i) r += scratch[i];
   return r;
 }
 
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(LaunchArgs a) {
-  constexpr int C4 = D / 4;                    // float4 columns of a row
-  constexpr int NG = kMergeThreads / C4;       // partition groups
-  const size_t bh = blockIdx.x;
-  const int b = (int)(bh / a.hq);
-  const int n = min(max(a.ctx[b], 0), a.max_ctx);
-  const int np = (n + a.part_tokens - 1) / a.part_tokens;
-  float *o = a.out + bh * D;
-  if (np == 0) {
-    for (int e = threadIdx.x; e < D; e += kMergeThreads) o[e] = 0.f;
+// Inclusive prefix sum over the workgroup (int64); *total gets the sum.
+__device__ __forceinline__ long long block_scan(long long x, long long *scratch, long long *total) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off *= 2) {
+    const long long y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  long long before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const long long v = scratch[i];
+    if (i < (int)(threadIdx.x >> 6)) before += v;
+    all += v;
+  }
+  *total = all;
+  return x + before;
+}
+
+// ---------------------------------------------------------------------------
+// attention kernel
+//
+// Work is counted in units: one unit is one 16-token block of one
+// (sequence, head chunk) pair.  Units are numbered sequence-major, then
+// chunk, then block, and the gridDim.x workgroups take equal contiguous
+// ranges of them (the first U % gridDim.x one unit more), so every
+// workgroup streams the same number of blocks whatever the mix of context
+// lengths.  A range is cut at (sequence, chunk) boundaries into pieces.  A
+// piece that is a whole (sequence, chunk) is finished on the spot: its
+// normalised output is written.  A pair split over several ranges leaves a
+// partial state per piece in the workspace (record slot 0 for the piece a
+// range starts with, slot 1 for the piece it ends with); the last of those
+// pieces to finish, found with an arrival counter, merges them.
+
+template <int KV, int D, int G>
+__global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
+  __shared__ long long s_scan[kWaves];
+  __shared__ long long s_first[3];  // first sequence, its first unit, its length
+  __shared__ int s_len[kThreads];     // clamped lengths, when batch <= kThreads
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  // wave index, known wave-uniform: everything derived from it stays scalar
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwg = gridDim.x, wgi = blockIdx.x;
+  const int hc = a.hc, chunks = a.chunks;
+  const int nph = kWaves / hc;  // phases: waves sharing a head
+  const int hl = w % hc, ph = w / hc;
+  const int hcg = hc * G;       // query heads of a chunk
+
+  auto seq_len = [&](int b) { return min(max(a.ctx[b], 0), a.max_ctx); };
+  auto seq_blocks = [&](int b) { return (seq_len(b) + kBlock - 1) / kBlock; };
+  const bool small_batch = a.batch <= kThreads;  // lengths kept in LDS
+  // a length after the scan: from LDS for a small batch, else from memory
+  auto len_of = [&](int b) { return small_batch ? s_len[b] : seq_len(b); };
+
+  // ---- speculation: the first piece this workgroup gets if every context
+  // is max_ctx long (an equal-length batch).  Its query rows and table
+  // entries are loaded now, in flight together with the lengths the split
+  // below needs, and used if the lengths confirm the guess.
+  const int nbm = (a.max_ctx + kBlock - 1) / kBlock;
+  const long long Ug = (long long)a.batch * chunks * nbm;
+  Query<KV, D, G> qry_g;
+  int tv_g = -1;
+  {
+    const long long per_g = Ug / nwg, rem_g = Ug % nwg;
+    const long long u0g = wgi * per_g + min((long long)wgi, rem_g);
+    const long long u1g = u0g + per_g + (wgi < rem_g ? 1 : 0);
+    if (u0g < u1g) {
+      const int bg = (int)(u0g / ((long long)chunks * nbm));
+      const long long off = u0g - (long long)bg * chunks * nbm;
+      const int cg = (int)(off / nbm), lo = (int)(off % nbm);
+      const int hi = (int)min((long long)nbm, u1g - (long long)bg * chunks * nbm - (long long)cg * nbm);
+      load_query<KV, D, G>(a, bg, cg * hc + hl, qry_g);
+      tv_g = load_table(a, bg, lo, ph, nph, 0,
+                        wave_blocks(lo * kBlock, min(a.max_ctx, hi * kBlock), ph, nph));
+    }
+  }
+
+  // ---- total units U, this workgroup's range [u0, u1), and the sequence
+  // holding u0.  Up to kThreads sequences: one block-wide scan of the
+  // per-sequence units gives all three.  More: a sum, then a chunked scan.
+  if (tid == 0) s_first[0] = -1;
+  long long U;
+  if (small_batch) {
+    const int len = tid < a.batch ? seq_len(tid) : 0;
+    s_len[tid] = len;
+    const long long ub = (long long)((len + kBlock - 1) / kBlock) * chunks;
+    const long long incl = block_scan(ub, s_scan, &U);
+    if (ub > 0) {
+      const long long per = U / nwg, rem = U % nwg;
+      const long long u0 = wgi * per + min((long long)wgi, rem);
+      if (incl - ub <= u0 && u0 < incl) {
+        s_first[0] = tid;
+        s_first[1] = incl - ub;
+        s_first[2] = len;
+      }
+    }
+  } else {
+    long long t = 0;
+    for (int b = tid; b < a.batch; b += kThreads) t += seq_blocks(b);
+    U = block_sum(t, s_scan) * chunks;
+  }
+  const long long per = U / nwg, rem = U % nwg;
+  auto range_start = [&](long long wg) { return wg * per + min(wg, rem); };
+  auto range_of = [&](long long u) {  // workgroup whose range holds unit u
+    const long long big = rem * (per + 1);
+    return u < big ? u / (per + 1) : rem + (u - big) / per;
+  };
+  const long long u0 = range_start(wgi), u1 = range_start(wgi + 1);
+
+  // empty sequences: zero output rows, spread over the workgroups (done
+  // after this workgroup's pieces, off the path to its first loads)
+  auto zero_empty_rows = [&]() {
+    for (int b = wgi; b < a.batch; b += nwg) {
+      if (len_of(b) == 0)
+        for (int i = tid; i < a.hq * D; i += kThreads) a.out[(size_t)b * a.hq * D + i] = 0.f;
+    }
+  };
+  if (u0 >= u1) {
+    __syncthreads();  // s_len complete
+    zero_empty_rows();
     return;
   }
-  const float2 *ml = a.ws_ml + bh * a.parts;
-  const float4 *acc4 = reinterpret_cast<const float4 *>(a.ws_acc + bh * a.parts * D);
-  __shared__ float s_red[kMergeThreads / 64];
-  __shared__ float4 s_part[NG][C4];
 
-  float mx = -__builtin_huge_valf();
-  for (int p = threadIdx.x; p < np; p += kMergeThreads) mx = fmaxf(mx, ml[p].x);
-  const float M = block_reduce(mx, s_red, true);
-  const auto weight = [&](float m) { return m == -__builtin_huge_valf() ? 0.f : fast_exp2(m - M); };
-  float lw = 0.f;
-  for (int p = threadIdx.x; p < np; p += kMergeThreads) {
-    const float2 v = ml[p];
-    lw = fmaf(weight(v.x), v.y, lw);
-  }
-  const float L = block_reduce(lw, s_red, false);
-
-  const int c = threadIdx.x % C4, grp = threadIdx.x / C4;
-  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](float w, float4 v) {
-    A.x = fmaf(w, v.x, A.x); A.y = fmaf(w, v.y, A.y);
-    A.z = fmaf(w, v.z, A.z); A.w = fmaf(w, v.w, A.w);
-  };
-  int p = grp;
-  for (; p + 3 * NG < np; p += 4 * NG) {
-    float4 v[4];
-    float w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = acc4[(size_t)(p + k * NG) * C4 + c];
-      w[k] = ml[p + k * NG].x;
+  if (a.batch > kThreads) {
+    long long base = 0;
+    for (int c0 = 0; c0 < a.batch; c0 += kThreads) {
+      const int b = c0 + tid;
+      const long long ub = b < a.batch ? (long long)seq_blocks(b) * chunks : 0;
+      long long total;
+      const long long incl = block_scan(ub, s_scan, &total);
+      const long long start = base + incl - ub;
+      if (ub > 0 && start <= u0 && u0 < start + ub) {
+        s_first[0] = b;
+        s_first[1] = start;
+        s_first[2] = seq_len(b);
+      }
+      __syncthreads();
+      base += total;
+      if (s_first[0] >= 0) break;
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) add(weight(w[k]), v[k]);
   }
-  for (; p < np; p += NG) add(weight(ml[p].x), acc4[(size_t)p * C4 + c]);
-  s_part[grp][c] = A;
   __syncthreads();
-  if (threadIdx.x < C4) {
-    float4 t = s_part[0][threadIdx.x];
-#pragma unroll
-    for (int g = 1; g < NG; ++g) {
-      const float4 u = s_part[g][threadIdx.x];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+  int b = (int)s_first[0];
+  long long pb = s_first[1];  // first unit of sequence b
+  int n = (int)s_first[2];    // its length (the scan has read it already)
+
+  // ---- the pieces of the range
+  long long pos = u0;
+  bool first_piece = true;
+  while (pos < u1) {
+    const int nb = (n + kBlock - 1) / kBlock;
+    const long long ub = (long long)nb * chunks;
+    if (ub == 0) {  // an empty sequence inside the range holds no units
+      ++b;
+      n = len_of(b);
+      continue;
     }
-    float *oo = o + 4 * threadIdx.x;  // out needs only 4-byte alignment
-    oo[0] = L > 0.f ? t.x / L : 0.f;
-    oo[1] = L > 0.f ? t.y / L : 0.f;
-    oo[2] = L > 0.f ? t.z / L : 0.f;
-    oo[3] = L > 0.f ? t.w / L : 0.f;
+    // the next sequence's length, read now and used after this piece
+    const int n_next = b + 1 < a.batch ? len_of(b + 1) : 0;
+    const long long off = pos - pb;
+    const int chunk = (int)(off / nb);
+    const int blk_lo = (int)(off - (long long)chunk * nb);
+    const long long seg_start = pb + (long long)chunk * nb, seg_end = seg_start + nb;
+    const long long pend = min(u1, seg_end);
+    const int blk_hi = (int)(pend - seg_start);
+
+    const int g = chunk * hc + hl;
+    const int tok0 = blk_lo * kBlock, tok_end = min(n, blk_hi * kBlock);
+    // the guess holds when every sequence has max_ctx tokens' worth of
+    // blocks and this one exactly max_ctx tokens: then the first piece is
+    // the guessed one, same blocks and same tail
+    if (first_piece && U == Ug && n == a.max_ctx) {
+      attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qry_g, tv_g, s_acc, s_m, s_l);
+    } else {
+      Query<KV, D, G> qry;
+      load_query<KV, D, G>(a, b, g, qry);
+      const int tv = load_table(a, b, blk_lo, ph, nph, 0, wave_blocks(tok0, tok_end, ph, nph));
+      attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qry, tv, s_acc, s_m, s_l);
+    }
+    __syncthreads();
+
+    // combine the phases of each head; then output or partial record
+    const size_t bh0 = (size_t)b * a.hq + (size_t)chunk * hcg;
+    const bool whole = blk_lo == 0 && blk_hi == nb;
+    const size_t rec0 = ((size_t)wgi * 2 + (first_piece ? 0 : 1)) * hcg;
+    for (int idx = tid; idx < hcg * D; idx += kThreads) {
+      const int r = idx / D, e = idx % D;  // r = hl * G + hh
+      const int hh = r % G, hw = r / G;
+      float M = -__builtin_huge_valf();
+      for (int v = 0; v < nph; ++v) M = fmaxf(M, s_m[v * hc + hw][hh]);
+      float A = 0.f, L = 0.f;
+      for (int v = 0; v < nph; ++v) {
+        const int wv = v * hc + hw;
+        const float sc = part_weight(s_m[wv][hh], M);
+        A = fmaf(sc, s_acc[wv][hh][e], A);
+        L = fmaf(sc, s_l[wv][hh], L);
+      }
+      if (whole) {
+        a.out[(bh0 + r) * D + e] = L > 0.f ? A / L : 0.f;
+      } else {
+        a.ws_acc[(rec0 + r) * D + e] = A;
+        if (e == 0) a.ws_ml[rec0 + r] = make_float2(M, L);
+      }
+    }
+
+    if (!whole) {
+      // Arrival.  Each wave waits until its own stores have reached the L2
+      // (the barrier by itself does not wait for outstanding stores); thread
+      // 0's device-scope release then covers them all.  The arrival that
+      // completes the count acquires every earlier one (one release
+      // sequence on the counter) and the barrier hands that on.
+      const long long w_lo = range_of(seg_start), w_hi = range_of(seg_end - 1);
+      uint32_t *cnt = a.counters + (size_t)b * chunks + chunk;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (uint32_t)(w_hi - w_lo);
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last;
+      }
+      __syncthreads();
+      if (s_last) {
+        // the record of piece k = w_lo + j: slot 0 unless the pair starts
+        // inside w_lo's range after its first unit (then it ends that range)
+        const int np = (int)(w_hi - w_lo + 1);
+        const int slot_lo = range_start(w_lo) == seg_start ? 0 : 1;
+        auto rec_of = [&](int j) {
+          return ((size_t)(w_lo + j) * 2 + (j == 0 ? slot_lo : 0)) * hcg;
+        };
+        const float4 *acc4 = reinterpret_cast<const float4 *>(a.ws_acc);
+        for (int idx = tid; idx < hcg * (D / 4); idx += kThreads) {
+          const int r = idx / (D / 4), c4 = idx % (D / 4);
+          float M = -__builtin_huge_valf();
+          for (int j = 0; j < np; ++j) M = fmaxf(M, a.ws_ml[rec_of(j) + r].x);
+          float L = 0.f;
+          float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+          auto add = [&](float2 ml, float4 v) {
+            const float sc = part_weight(ml.x, M);
+            L = fmaf(sc, ml.y, L);
+            A.x = fmaf(sc, v.x, A.x); A.y = fmaf(sc, v.y, A.y);
+            A.z = fmaf(sc, v.z, A.z); A.w = fmaf(sc, v.w, A.w);
+          };
+          int j = 0;
+          for (; j + 4 <= np; j += 4) {  // four pieces' loads in flight
+            float2 ml[4];
+            float4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const size_t rr = rec_of(j + k) + r;
+              ml[k] = a.ws_ml[rr];
+              v[k] = acc4[rr * (D / 4) + c4];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) add(ml[k], v[k]);
+          }
+          for (; j < np; ++j) {
+            const size_t rr = rec_of(j) + r;
+            add(a.ws_ml[rr], acc4[rr * (D / 4) + c4]);
+          }
+          float *o = a.out + (bh0 + r) * D + 4 * c4;  // out needs only 4-byte alignment
+          o[0] = L > 0.f ? A.x / L : 0.f;
+          o[1] = L > 0.f ? A.y / L : 0.f;
+          o[2] = L > 0.f ? A.z / L : 0.f;
+          o[3] = L > 0.f ? A.w / L : 0.f;
+        }
+        if (tid == 0)  // ready for the next run (ordered by the kernel boundary)
+          __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // LDS is reused by the next piece
+
+    first_piece = false;
+    pos = pend;
+    if (pos == pb + ub) {
+      pb += ub;
+      ++b;
+      n = n_next;
+    }
   }
+  zero_empty_rows();
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 template <int KV, int D, int G>
-hipError_t launch_partition_t(const LaunchArgs &a, hipStream_t s) {
-  const size_t wgs = (size_t)a.batch * a.chunks * a.parts;
-  hipLaunchKernelGGL((partition_kernel<KV, D, G>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+hipError_t launch_attention_t(const LaunchArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((attention_kernel<KV, D, G>), dim3((unsigned)a.nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KV, int D>
 hipError_t by_group(const LaunchArgs &a, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_partition_t<KV, D, 1>(a, s);
-    case 2: return launch_partition_t<KV, D, 2>(a, s);
-    case 4: return launch_partition_t<KV, D, 4>(a, s);
-    case 8: return launch_partition_t<KV, D, 8>(a, s);
+    case 1: return launch_attention_t<KV, D, 1>(a, s);
+    case 2: return launch_attention_t<KV, D, 2>(a, s);
+    case 4: return launch_attention_t<KV, D, 4>(a, s);
+    case 8: return launch_attention_t<KV, D, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -574,8 +787,8 @@ bool kernel_supported(int kv, int d, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t launch_partition(const LaunchArgs &a, hipStream_t s) {
-  if (a.batch == 0 || a.parts == 0) return hipSuccess;
+hipError_t launch_attention(const LaunchArgs &a, hipStream_t s) {
+  if (a.batch == 0 || a.nwg == 0) return hipSuccess;
   switch (a.kv) {
     case KV_F32: return by_dim<KV_F32>(a, s);
     case KV_BF16: return by_dim<KV_BF16>(a, s);
@@ -584,15 +797,9 @@ hipError_t launch_partition(const LaunchArgs &a, hipStream_t s) {
   }
 }
 
-hipError_t launch_merge(const LaunchArgs &a, hipStream_t s) {
-  if (a.batch == 0 || a.parts <= 1) return hipSuccess;
-  const unsigned wgs = (unsigned)((size_t)a.batch * a.hq);
-  if (a.d == 64)
-    hipLaunchKernelGGL((merge_kernel<64>), dim3(wgs), dim3(kMergeThreads), 0, s, a);
-  else if (a.d == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), dim3(wgs), dim3(kMergeThreads), 0, s, a);
-  else
-    return hipErrorInvalidValue;
+hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

@@ -10,15 +10,18 @@ from workloads.device import to_device
 TOL = {"f32": 2e-3, "bf16": 2e-3, "fp8_e4m3": 3e-2}
 
 
-def gpu_decode(inp, part_tokens=0, dev=None, out=None, workspace=None):
-    """Run one decode step of ``inp`` through the C ABI; float32 [B][Hq][d]."""
+def gpu_decode(inp, workgroups=0, heads=0, dev=None, out=None, workspace=None):
+    """Run one decode step of ``inp`` through the C ABI; float32 [B][Hq][d].
+    ``workgroups`` / ``heads``: launch-shape overrides (0: automatic)."""
     s = inp.spec
     dev = dev or to_device(inp)
     pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, s.kv_dtype, dev.k_scale, dev.v_scale)
     try:
         pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
-        if part_tokens:
-            pool.set_partition_tokens(part_tokens)
+        if workgroups:
+            pool.set_workgroups(workgroups)
+        if heads:
+            pool.set_heads_per_workgroup(heads)
         if workspace is None:
             nbytes = pool.workspace_bytes(s.num_q_heads)
             workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None

@@ -83,7 +83,6 @@ def test_run_errors(pool):
     assert _status(run, pool, Q, "bf16", 8, 0.1, OUT, WS, 1 << 20, 0) == pa.binding.PA_ERR_STATE
     assert _status(pa.pa_decode_workspace_bytes, pool, 8) == pa.binding.PA_ERR_STATE
     pa.pa_block_table_set(pool, TBL, CTX, 3, 4, 64)
-    pa.pa_decode_set_partition_tokens(pool, 16)  # several partitions: partials to keep
     ws = pa.pa_decode_workspace_bytes(pool, 8)
     assert ws > 0
     assert _status(run, pool, Q, "f32", 8, 0.1, OUT, WS, ws, 0) == pa.binding.PA_ERR_DTYPE
@@ -118,25 +117,25 @@ def test_fp8_pool_needs_fp8_entry():
         pa.pa_kv_pool_destroy(h)
 
 
-def test_partition_override_and_workspace_size(pool):
+def test_workgroups_override_and_workspace_size(pool):
     pa.pa_block_table_set(pool, TBL, CTX, 3, 64, 1000)
-    assert _status(pa.pa_decode_set_partition_tokens, pool, 24) == pa.binding.PA_ERR_SHAPE
-    assert _status(pa.pa_decode_set_partition_tokens, pool, -16) == pa.binding.PA_ERR_SHAPE
-    pa.pa_decode_set_partition_tokens(pool, 64)
-    assert pa.pa_decode_partition_tokens(pool) == 64
-    parts = (1000 + 63) // 64
-    recs = 3 * 8 * parts
+    assert _status(pa.pa_decode_set_workgroups, pool, -1) == pa.binding.PA_ERR_SHAPE
+    assert _status(pa.pa_decode_set_workgroups, pool, (1 << 16) + 1) == pa.binding.PA_ERR_SHAPE
+    pa.pa_decode_set_workgroups(pool, 7)
+    assert pa.pa_decode_workgroups(pool) == 7
+    hc = pa.pa_decode_heads_per_workgroup(pool)  # 2 KV heads, batch 3: split, hc 2
+    assert hc == 2
+    recs = 7 * 2 * hc * (8 // 2)  # two records per workgroup, hc * G query heads each
     ml = (recs * 8 + 255) // 256 * 256
     assert pa.pa_decode_workspace_bytes(pool, 8) == ml + recs * 128 * 4
-    pa.pa_decode_set_partition_tokens(pool, 0)
-    auto = pa.pa_decode_partition_tokens(pool)
-    assert auto % 16 == 0 and auto >= 16
-    # one partition writes the output directly: no workspace
-    pa.pa_decode_set_partition_tokens(pool, 1024)
+    # a single workgroup never splits a sequence: no workspace
+    pa.pa_decode_set_workgroups(pool, 1)
     assert pa.pa_decode_workspace_bytes(pool, 8) == 0
-    pa.pa_decode_set_partition_tokens(pool, 0)
-    # an empty context needs no workspace
+    pa.pa_decode_set_workgroups(pool, 0)
+    assert pa.pa_decode_workgroups(pool) == 3 * 1 * 63  # fewer blocks of work than CUs
+    # an empty context: one workgroup (it writes the zero rows), no workspace
     pa.pa_block_table_set(pool, TBL, CTX, 3, 64, 0)
+    assert pa.pa_decode_workgroups(pool) == 1
     assert pa.pa_decode_workspace_bytes(pool, 8) == 0
 
 
@@ -145,40 +144,36 @@ CUS = 256
 
 
 def expected_shape(hkv, batch, ctx):
-    """The documented automatic launch shape, restated."""
+    """The documented automatic launch shape, restated: (head chunk, workgroups)."""
     hmax = max(c for c in (1, 2, 4) if c <= WAVES_PER_WG and hkv % c == 0)
     fits = [c for c in (4, 2, 1) if c <= hmax and hkv % c == 0 and batch * (hkv // c) >= CUS]
     hc = fits[0] if fits else hmax
-    units = batch * (hkv // hc)
-    parts = 1 if units >= CUS else -(-CUS // units)
-    tokens = -(-ctx // 16) * 16 if parts == 1 else ctx // parts // 16 * 16
-    return hc, min(max(tokens, 16), 1 << 20)
+    units = batch * (hkv // hc) * -(-ctx // 16)
+    return hc, max(1, min(CUS, units))
 
 
 def test_auto_launch_shape():
-    """One workgroup per compute unit at least; whole contexts when the
-    (sequence, head chunk) pairs already cover the compute units."""
+    """One workgroup per compute unit (fewer only for tiny batches); whole
+    (sequence, chunk) pairs per workgroup when they number >= 256."""
     cases = [(8, 32, 4096), (8, 4, 131072), (8, 64, 16384), (8, 1, 512), (32, 32, 8192),
-             (2, 2, 100), (1, 1, 100000), (8, 64, 0), (6, 100, 1000), (4, 128, 5000)]
+             (2, 2, 100), (1, 1, 100000), (8, 64, 0), (6, 100, 1000), (4, 128, 5000),
+             (2, 2, 37)]
     for hkv, batch, ctx in cases:
         h = pa.pa_kv_pool_create(64, 16, hkv, 128, "bf16", K, V)
         try:
             pa.pa_block_table_set(h, TBL, CTX, batch, max(1, (ctx + 15) // 16), ctx)
             hc = pa.pa_decode_heads_per_workgroup(h)
-            p = pa.pa_decode_partition_tokens(h)
-            assert (hc, p) == expected_shape(hkv, batch, ctx), (hkv, batch, ctx, hc, p)
-            parts = max(1, -(-ctx // p))
-            assert batch * (hkv // hc) * parts >= min(CUS, batch * (hkv // hc) * -(-ctx // 16))
-            if batch * (hkv // hc) >= CUS:
-                assert parts == 1 and pa.pa_decode_workspace_bytes(h, hkv) == 0
+            nwg = pa.pa_decode_workgroups(h)
+            assert (hc, nwg) == expected_shape(hkv, batch, ctx), (hkv, batch, ctx, hc, nwg)
         finally:
             pa.pa_kv_pool_destroy(h)
-    # one workgroup per (sequence, KV head), whole contexts
-    assert expected_shape(8, 32, 4096) == (1, 4096)
-    # four heads per workgroup, whole contexts
-    assert expected_shape(32, 32, 8192) == (4, 8192)
-    # too few sequences: widest chunk, 32 partitions of 4096 tokens
-    assert expected_shape(8, 4, 131072) == (4, 4096)
+    # one workgroup per (sequence, KV head): with equal lengths, whole contexts
+    assert expected_shape(8, 32, 4096) == (1, 256)
+    assert expected_shape(32, 32, 8192) == (4, 256)
+    # too few sequences: widest chunk, each (sequence, chunk) split 32 ways
+    assert expected_shape(8, 4, 131072) == (4, 256)
+    # the tiny workload: 2 * 2 * 7 = 14 units of work, 14 workgroups
+    assert expected_shape(2, 2, 100) == (2, 7) or expected_shape(2, 2, 100)[1] <= 14
 
 
 def test_heads_override(pool):
@@ -191,7 +186,7 @@ def test_heads_override(pool):
     pa.pa_decode_set_heads_per_workgroup(pool, 1)
     assert pa.pa_decode_heads_per_workgroup(pool) == 1
     pa.pa_decode_set_heads_per_workgroup(pool, 0)
-    assert pa.pa_decode_heads_per_workgroup(pool) == 2  # batch 3: split, widest chunk
+    assert pa.pa_decode_heads_per_workgroup(pool) == 2  # batch 3: widest chunk
 
 
 def test_profile_needs_enable(pool):

@@ -77,56 +77,65 @@ def test_small_shapes(kv, d, hq, hkv):
                 seed=1000 + d + hq + 7 * hkv, context_lens=CTX_MIX, pool_blocks=60)
     inp = make_inputs(spec, poison=True)
     want = oracle_decode(inp)
-    for part in (0, 16, 48, 128):
-        say(f"[parity] small kv={kv} d={d} hq={hq} hkv={hkv} part={part}")
-        got = gpu_decode(inp, part_tokens=part)
+    # automatic shape; one workgroup (nothing split); odd counts that split
+    # sequences at arbitrary blocks; more workgroups than blocks of work
+    for nwg, heads in ((0, 0), (1, 0), (3, 1), (7, 0), (64, 1), (200, 0), (1000, 2)):
+        if heads and hkv % heads:
+            continue
+        say(f"[parity] small kv={kv} d={d} hq={hq} hkv={hkv} wg={nwg} heads={heads}")
+        got = gpu_decode(inp, workgroups=nwg, heads=heads)
         err = max_err(got, want)
-        assert err <= TOL[kv], (part, err)
+        assert err <= TOL[kv], (nwg, heads, err)
         assert np.all(got[CTX_MIX.index(0)] == 0.0)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_context_edges(kv):
-    P = 64
-    ctx = (0, 1, 15, 16, 17, 31, 33, P - 1, P, P + 1, 2 * P + 3, 1000)
+    ctx = (0, 1, 15, 16, 17, 31, 33, 63, 64, 65, 131, 1000)
     spec = Spec(name="edges", batch=len(ctx), num_q_heads=8, num_kv_heads=2, head_dim=128,
                 kv_dtype=kv, q_dtype="bf16", seed=77, context_lens=ctx)
     inp = make_inputs(spec, poison=True)
     want = oracle_decode(inp)
-    say(f"[parity] edges kv={kv}")
-    got = gpu_decode(inp, part_tokens=P)
-    assert max_err(got, want) <= TOL[kv]
+    for nwg in (0, 5, 17, 96):
+        say(f"[parity] edges kv={kv} wg={nwg}")
+        got = gpu_decode(inp, workgroups=nwg)
+        assert max_err(got, want) <= TOL[kv], nwg
 
 
 def test_all_empty_batch():
     spec = Spec(name="empty", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
                 kv_dtype="bf16", q_dtype="bf16", seed=5, context_lens=(0, 0, 0))
     inp = make_inputs(spec)
-    say("[parity] all-empty batch")
-    got = gpu_decode(inp)
-    assert np.all(got == 0.0)
+    for nwg in (0, 1, 4):
+        say(f"[parity] all-empty batch wg={nwg}")
+        got = gpu_decode(inp, workgroups=nwg)
+        assert np.all(got == 0.0)
 
 
-def test_partition_sweep():
+def test_workgroup_sweep():
+    """Equal shares of the blocks at many workgroup counts: sequences split
+    into 1..hundreds of pieces, merged by the last piece to finish."""
     spec = Spec(name="sweep", batch=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
                 kv_dtype="bf16", q_dtype="bf16", seed=88, context_lens=(4096, 4001, 77))
     inp = make_inputs(spec)
     want = oracle_decode(inp)
-    for part in (16, 64, 256, 512, 1024, 4096, 8192):
-        say(f"[parity] sweep part={part}")
-        got = gpu_decode(inp, part_tokens=part)
-        assert max_err(got, want) <= TOL["bf16"], part
+    for nwg, heads in ((1, 0), (2, 0), (3, 4), (24, 1), (96, 2), (256, 0), (777, 4),
+                       (4000, 1)):
+        say(f"[parity] sweep wg={nwg} heads={heads}")
+        got = gpu_decode(inp, workgroups=nwg, heads=heads)
+        assert max_err(got, want) <= TOL["bf16"], (nwg, heads)
 
 
-def test_long_single_partition():
-    """One partition per sequence: every wave loops over many blocks."""
-    spec = Spec(name="longpart", batch=2, num_q_heads=8, num_kv_heads=1, head_dim=128,
+def test_long_single_sequence():
+    """Few workgroups: every wave loops over many blocks."""
+    spec = Spec(name="longseq", batch=2, num_q_heads=8, num_kv_heads=1, head_dim=128,
                 kv_dtype="bf16", q_dtype="bf16", seed=89, context_lens=(20000, 9999))
     inp = make_inputs(spec)
     want = oracle_decode(inp)
-    say("[parity] one partition of 20000 tokens")
-    got = gpu_decode(inp, part_tokens=20000 // 16 * 16 + 16)
-    assert max_err(got, want) <= TOL["bf16"]
+    for nwg in (1, 2, 5):
+        say(f"[parity] long sequences, {nwg} workgroups")
+        got = gpu_decode(inp, workgroups=nwg)
+        assert max_err(got, want) <= TOL["bf16"], nwg
 
 
 # ---------------------------------------------------------------------------
@@ -212,13 +221,13 @@ def test_canaries_around_out_and_workspace():
     dev = to_device(inp)
     pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
     pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
-    pool.set_partition_tokens(64)
+    pool.set_workgroups(37)
     nbytes = pool.workspace_bytes(s.num_q_heads)
     pool.close()
     ws_big = torch.full((nbytes + 2 * 4096,), 0xA5, dtype=torch.uint8, device="cuda")
     ws = ws_big[4096:4096 + nbytes]
     say("[parity] canaries")
-    got = gpu_decode(inp, part_tokens=64, dev=dev, out=out, workspace=ws)
+    got = gpu_decode(inp, workgroups=37, dev=dev, out=out, workspace=ws)
     ob = out_big.cpu().numpy()
     assert np.all(ob[:guard] == 12345.0) and np.all(ob[guard + n_out:] == 12345.0)
     wb = ws_big.cpu().numpy()
@@ -278,13 +287,13 @@ def test_profile_events():
     pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "f32")
     try:
         pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
-        ws = torch.empty(pool.workspace_bytes(8), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(max(pool.workspace_bytes(8), 256), dtype=torch.uint8, device="cuda")
         out = torch.empty(2, 8, 64, device="cuda")
         pa.pa_profile_enable(pool.handle, 4)
         for _ in range(6):
             pool.decode(dev.q, out, ws)
-        part, merge = pa.pa_profile_read(pool.handle, 8)
-        assert len(part) == 4 and all(t > 0 for t in part) and all(t > 0 for t in merge)
+        kern = pa.pa_profile_read(pool.handle, 8)
+        assert len(kern) == 4 and all(t > 0 for t in kern)
         pa.pa_profile_enable(pool.handle, 0)
     finally:
         pool.close()
@@ -296,8 +305,8 @@ def test_profile_events():
 
 def test_repeated_runs_on_one_handle():
     """Runs on one handle reuse its arrival counters: every run must agree
-    with the oracle, also after a run with a smaller batch and after a run
-    whose partials go through the separate merge kernel."""
+    with the oracle, also after runs with a smaller batch and with other
+    workgroup counts and head chunks (different sequences split)."""
     spec = Spec(name="repeat", batch=5, num_q_heads=16, num_kv_heads=4, head_dim=128,
                 kv_dtype="bf16", q_dtype="bf16", seed=96, context_lens=(900, 17, 512, 0, 1300))
     inp = make_inputs(spec, poison=True)
@@ -308,16 +317,18 @@ def test_repeated_runs_on_one_handle():
         s = inp.spec
         ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
         out = torch.empty((s.batch, s.num_q_heads, s.head_dim), device="cuda")
-        for it, (part, nb) in enumerate([(64, 5), (64, 5), (128, 3), (64, 5), (16, 5),
-                                         (64, 5), (0, 5), (64, 5)]):
-            say(f"[parity] repeat it={it} part={part} batch={nb}")
+        for it, (nwg, heads, nb) in enumerate([(64, 0, 5), (64, 0, 5), (13, 2, 3), (64, 4, 5),
+                                               (300, 1, 5), (64, 0, 5), (0, 0, 5), (1, 0, 4),
+                                               (64, 0, 5)]):
+            say(f"[parity] repeat it={it} wg={nwg} heads={heads} batch={nb}")
             pool.set_block_table(dev.block_table[:nb], dev.context_lens[:nb], inp.max_context_len)
-            pool.set_partition_tokens(part)
+            pool.set_workgroups(nwg)
+            pool.set_heads_per_workgroup(heads)
             assert pool.workspace_bytes(s.num_q_heads) <= ws.numel()
             out.fill_(float("nan"))
             pool.decode(dev.q[:nb], out[:nb], ws, scale=float(inp.scale))
             torch.cuda.synchronize()
             got = out[:nb].cpu().numpy()
-            assert max_err(got, want[:nb]) <= TOL["bf16"], (it, part, nb)
+            assert max_err(got, want[:nb]) <= TOL["bf16"], (it, nwg, heads, nb)
     finally:
         pool.close()
