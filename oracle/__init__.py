@@ -28,3 +28,9 @@ from .decode_attention import (  # noqa: F401
     paged_decode_attention,
 )
 from .kv_size import kv_cache_bytes  # noqa: F401
+from .cache_write import (  # noqa: F401
+    E4M3FN_MAX,
+    append_new_tokens,
+    e4m3fn_encode,
+    quantize_row,
+)

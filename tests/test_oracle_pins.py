@@ -438,3 +438,127 @@ def test_planted_mistakes_are_caught(mutant, monkeypatch):
             except Exception:  # an assertion or a crash: the pin noticed
                 broken.append(pin.__name__)
     assert broken, f"no pin catches the planted mistake {mutant!r}"
+
+
+# ---------------------------------------------------------------------------
+# pins of the cache write (the new token's K/V into its slot; FP8 on write)
+
+
+def test_e4m3fn_encode_matches_torch_cast():
+    """Nearest-even encoding against torch's own float8_e4m3fn cast."""
+    rng = _rng(11)
+    y = np.concatenate([
+        rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 3,
+        rng.standard_normal(5000) * 2.0 ** -8,  # subnormal range
+        oracle.E4M3FN_TABLE[:0x7F], -oracle.E4M3FN_TABLE[1:0x7F],
+    ]).astype(np.float32)
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3fn_encode(y)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3fn_encode_ties_to_even():
+    """Midpoints between neighbouring codes go to the even code."""
+    v = oracle.E4M3FN_TABLE
+    for c in range(0, 0x7E):
+        mid = (v[c] + v[c + 1]) / 2  # exact in float64
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3fn_encode(np.array([mid]))[0] == even, c
+        assert oracle.e4m3fn_encode(np.array([-mid]))[0] == (even | 0x80), c
+        # just off the midpoint goes to the nearer code
+        assert oracle.e4m3fn_encode(np.array([np.nextafter(mid, 0)]))[0] == c
+        assert oracle.e4m3fn_encode(np.array([np.nextafter(mid, 1000)]))[0] == c + 1
+
+
+def test_quantize_row_scale_and_bound():
+    """Scale = absmax/448 in float32; the absmax element is +-448 exactly;
+    zero rows get scale 1; every value is within half an E4M3 step of
+    x/scale (relative 2^-4 for normals, 2^-10 absolute in the subnormals)."""
+    rng = _rng(12)
+    for trial in range(200):
+        x = (rng.standard_normal(128) * 10.0 ** rng.uniform(-6, 4)).astype(np.float32)
+        codes, sc = oracle.quantize_row(x)
+        assert sc == np.float32(np.max(np.abs(x))) / np.float32(448)
+        i = int(np.argmax(np.abs(x)))
+        assert oracle.E4M3FN_TABLE[codes[i]] == 448.0 * np.sign(x[i])
+        y = np.clip(x.astype(np.float64) / np.float64(sc), -448, 448)
+        dq = oracle.E4M3FN_TABLE[codes]
+        bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10)
+        assert np.all(np.abs(dq - y) <= bound + 1e-12 * np.abs(y)), trial
+    codes, sc = oracle.quantize_row(np.zeros(64, np.float32))
+    assert sc == 1.0 and np.all(codes == 0)
+
+
+def test_quantize_row_matches_the_input_fixture():
+    """The write quantiser and the (torch) quantiser that produced the FP8
+    workloads agree code for code and scale for scale."""
+    from workloads.synthetic import _to_fp8
+    x = _rng(13).standard_normal((3, 16, 2, 128)).astype(np.float32)
+    codes, scales = _to_fp8(x)
+    for n in range(3):
+        for s in range(16):
+            for g in range(2):
+                c, sc = oracle.quantize_row(x[n, s, g])
+                assert np.array_equal(c, codes[n, s, g]) and sc == scales[n, g, s]
+
+
+def test_append_writes_exactly_the_new_slots():
+    """Only row (table[b][(n-1)//16], (n-1)%16, g) changes, for every b with
+    n > 0 and every KV head g; empty sequences and other slots keep their
+    bytes."""
+    for kv in ("f32", "bf16", "fp8_e4m3"):
+        spec = Spec(name="app", batch=5, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                    kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", seed=21,
+                    context_lens=(1, 16, 17, 0, 40))
+        inp = make_inputs(spec, poison=True)
+        rng = _rng(22)
+        x_k = rng.standard_normal((5, 2, 64)).astype(np.float32)
+        x_v = rng.standard_normal((5, 2, 64)).astype(np.float32)
+        if kv == "bf16":
+            kn = torch.from_numpy(x_k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            vn = torch.from_numpy(x_v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        else:
+            kn, vn = x_k, x_v
+        k2, v2, ks2, vs2 = oracle.append_new_tokens(
+            inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens, kn, vn, kv,
+            inp.k_scale, inp.v_scale)
+        changed = np.zeros(inp.k_pool.shape[:3], bool)
+        for b, n in enumerate(inp.context_lens):
+            if n == 0:
+                continue
+            t = n - 1
+            p, o = inp.block_table[b, t // 16], t % 16
+            changed[p, o, :] = True
+            if kv == "fp8_e4m3":
+                for g in range(2):
+                    c, sc = oracle.quantize_row(x_k[b, g])
+                    assert np.array_equal(k2[p, o, g], c) and ks2[p, g, o] == sc
+            else:
+                assert np.array_equal(k2[p, o], kn[b]) and np.array_equal(v2[p, o], vn[b])
+        same = lambda a, b: np.array_equal(a.view(np.uint8), b.view(np.uint8))  # NaN-safe
+        assert same(k2[~changed], inp.k_pool[~changed]) and same(v2[~changed], inp.v_pool[~changed])
+
+
+def test_append_then_attend_is_contiguous_attention():
+    """Append each new token, then attend: the result equals torch's float64
+    attention over the contiguous cache that includes the new token (the
+    decode step of [d7kj] section 六)."""
+    rng = _rng(23)
+    Hq, Hkv, d = 8, 2, 64
+    lens = [5, 16, 33]
+    pool = AppendOnlyPool(16, Hkv, d, rng)
+    cache_k = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    cache_v = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    for s, n in enumerate(lens):
+        for t in range(n - 1):  # all but the newest token are already cached
+            pool.append(s, cache_k[s][t], cache_v[s][t])
+        pool.append(s, np.full((Hkv, d), np.nan), np.full((Hkv, d), np.nan))  # its slot
+    table = pool.table(len(lens))
+    k_new = np.stack([cache_k[s][-1] for s in range(len(lens))])
+    v_new = np.stack([cache_v[s][-1] for s in range(len(lens))])
+    k2, v2, _, _ = oracle.append_new_tokens(pool.k, pool.v, table, lens, k_new, v_new, "f64")
+    q = rng.standard_normal((len(lens), Hq, d))
+    got = _oracle(q, k2, v2, table, lens, 0.125)
+    for s in range(len(lens)):
+        want = _sdpa(q[s], cache_k[s], cache_v[s], 0.125)
+        assert np.allclose(got[s], want, rtol=0, atol=1e-12)
