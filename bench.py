@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--heads-per-workgroup", type=int, default=0, help="0: automatic")
     ap.add_argument("--cold-iters", type=int, default=30,
                     help="extra steps timed after a 1 GiB cache flush each")
+    ap.add_argument("--append-iters", type=int, default=100,
+                    help="timed launches of the cache write (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -206,6 +208,29 @@ def main():
             ev1.synchronize()
             cold.append(ev0.elapsed_time(ev1) * 1e-3)
         del flush
+    # the write half of a decode step: each sequence's new token into the
+    # cache (one launch), timed on its own with HIP events
+    append = None
+    if args.append_iters > 0:
+        g = torch.Generator(device="cpu").manual_seed(398)
+        src_dtype = torch.float32 if s.kv_dtype == "f32" else torch.bfloat16
+        k_new = torch.randn((s.batch, s.num_kv_heads, s.head_dim), generator=g).to(src_dtype).cuda()
+        v_new = torch.randn((s.batch, s.num_kv_heads, s.head_dim), generator=g).to(src_dtype).cuda()
+        for _ in range(5):
+            pools[0].append(k_new, v_new)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.append_iters):
+            pools[0].append(k_new, v_new)
+        ev1.record()
+        ev1.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / args.append_iters
+        eb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[s.kv_dtype]
+        written = s.batch * s.num_kv_heads * (s.head_dim * eb + (4 if eb == 1 else 0)) * 2
+        append = {"us": round(us, 2), "bytes_written": written, "iters": args.append_iters,
+                  "note": "pa_cache_append of one new token per sequence, back-to-back launches"}
+        log(f"cache write: {us:.2f} us per launch")
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -258,6 +283,7 @@ def main():
             "note": "one step after reading 1 GiB elsewhere; event-timed step",
         },
         "cpu_baseline": cpu,
+        "cache_append": append,
     }
     print(json.dumps(res), flush=True)
     for p in pools:

@@ -88,7 +88,8 @@ typedef enum pa_status {
  *
  * k_cache, v_cache: device, [num_blocks][16][num_kv_heads][head_dim] of
  *   kv_dtype, each 16-byte aligned (the block pool of the d7kj.com page,
- *   section 三; layout of the qingdujian.com notes, section 二).
+ *   section 三; layout of the qingdujian.com notes, section 二).  Decode
+ *   runs only read them; pa_cache_append writes the new tokens' rows.
  * k_scale, v_scale: device, float32 [num_blocks][num_kv_heads][16] -- one
  *   scale per (block, KV head, slot), i.e. per token and head (d7kj.com
  *   page, section 四); the stored value is e4m3(code) * scale.  Required
@@ -99,9 +100,8 @@ typedef enum pa_status {
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED.
  */
 pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                            int32_t head_dim, pa_dtype kv_dtype, const void *k_cache,
-                            const void *v_cache, const float *k_scale, const float *v_scale,
-                            pa_kv_pool **out_pool);
+                            int32_t head_dim, pa_dtype kv_dtype, void *k_cache, void *v_cache,
+                            float *k_scale, float *v_scale, pa_kv_pool **out_pool);
 
 /* pa_kv_pool_destroy -- free the handle (NULL is ignored).  Device buffers
  * are untouched.  Work already enqueued is unaffected. */
@@ -140,6 +140,32 @@ pa_status pa_block_table_set(pa_kv_pool *pool, const int32_t *block_table,
  *   first offending sequence is named in pa_last_error), PA_ERR_HIP.
  */
 pa_status pa_block_table_validate(pa_kv_pool *pool, void *stream);
+
+/*
+ * pa_cache_append -- write each sequence's new token into the cache.
+ *
+ * The decode step appends the new token's key and value to its sequence's
+ * cache before attending (d7kj.com page, sections 一 and 六).  With the
+ * tables set last, the token of sequence b goes to position
+ * t = context_lens[b] - 1 (the new token is the last one counted; lengths
+ * above max_context_len are clamped to it): physical block
+ * block_table[b][t / 16], slot t % 16, one row per KV head.
+ * k_new, v_new: device [batch][num_kv_heads][head_dim] of src_dtype.
+ *   f32 and bf16 pools: src_dtype must be the pool's dtype; the rows are
+ *   stored as they are.
+ *   FP8 pool: src_dtype PA_DTYPE_F32 or PA_DTYPE_BF16; each (token, head)
+ *   row is quantised (d7kj.com page, section 四): scale = absmax / 448 in
+ *   float32 (1 for an all-zero row), code = nearest-even E4M3FN value of
+ *   clamp(x / scale, -448, 448) (IEEE float32 division), and the scale is
+ *   stored at k_scale / v_scale[block][head][slot].
+ * Sequences with context_lens[b] == 0 are skipped; block ids outside
+ * [0, num_blocks) are not written.  Asynchronous on `stream`; a decode run
+ * enqueued after it on the same stream sees the new rows.
+ * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_DTYPE,
+ *   PA_ERR_SHAPE, PA_ERR_HIP.
+ */
+pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new,
+                          pa_dtype src_dtype, void *stream);
 
 /*
  * pa_decode_workspace_bytes -- device scratch a decode run needs.

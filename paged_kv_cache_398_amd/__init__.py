@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     load_library,
     pa_block_table_set,
     pa_block_table_validate,
+    pa_cache_append,
     pa_decode_fp8_run,
     pa_decode_heads_per_workgroup,
     pa_decode_run,
@@ -66,6 +67,15 @@ class PagedKVPool:
 
     def heads_per_workgroup(self):
         return pa_decode_heads_per_workgroup(self.handle)
+
+    def append(self, k_new, v_new, stream=None):
+        """Write each sequence's new token (``k_new``/``v_new`` device
+        [B][Hkv][d]) at position context_lens[b] - 1 of the tables set last.
+        f32/bf16 pools take rows of their own dtype; an FP8 pool quantises
+        float32 or bfloat16 rows."""
+        import torch  # only for the dtype of the rows
+        src = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(k_new.dtype, self.kv_dtype)
+        pa_cache_append(self.handle, k_new, v_new, src, stream)
 
     def workspace_bytes(self, num_q_heads):
         return pa_decode_workspace_bytes(self.handle, num_q_heads)

@@ -29,6 +29,7 @@ SIGNATURES = [
     ("pa_kv_pool_destroy", None, [_vp]),
     ("pa_block_table_set", _i32, [_vp, _vp, _vp, _i32, _i32, _i32]),
     ("pa_block_table_validate", _i32, [_vp, _vp]),
+    ("pa_cache_append", _i32, [_vp, _vp, _vp, _i32, _vp]),
     ("pa_decode_workspace_bytes", _i32, [_vp, _i32, ctypes.POINTER(_sz)]),
     ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
@@ -125,6 +126,11 @@ def pa_block_table_set(pool, block_table, context_lens, batch, max_blocks_per_se
 
 def pa_block_table_validate(pool, stream=None) -> None:
     _check(load_library().pa_block_table_validate(pool, _stream(stream)))
+
+
+def pa_cache_append(pool, k_new, v_new, src_dtype, stream=None) -> None:
+    _check(load_library().pa_cache_append(pool, _ptr(k_new), _ptr(v_new), _dtype(src_dtype),
+                                          _stream(stream)))
 
 
 def pa_decode_workspace_bytes(pool, num_q_heads) -> int:

@@ -21,8 +21,8 @@
 struct pa_kv_pool {
   int32_t num_blocks = 0, num_kv_heads = 0, head_dim = 0;
   pa_dtype kv_dtype = PA_DTYPE_F32;
-  const void *k_cache = nullptr, *v_cache = nullptr;
-  const float *k_scale = nullptr, *v_scale = nullptr;
+  void *k_cache = nullptr, *v_cache = nullptr;
+  float *k_scale = nullptr, *v_scale = nullptr;
   // block tables of the current step
   bool table_set = false;
   const int32_t *block_table = nullptr, *context_lens = nullptr;
@@ -238,9 +238,8 @@ void release_events(pa_kv_pool *p) {
 extern "C" {
 
 pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                            int32_t head_dim, pa_dtype kv_dtype, const void *k_cache,
-                            const void *v_cache, const float *k_scale, const float *v_scale,
-                            pa_kv_pool **out_pool) {
+                            int32_t head_dim, pa_dtype kv_dtype, void *k_cache, void *v_cache,
+                            float *k_scale, float *v_scale, pa_kv_pool **out_pool) {
   if (!out_pool) return fail(PA_ERR_NULL, "out_pool is NULL");
   *out_pool = nullptr;
   if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "k_cache or v_cache is NULL");
@@ -353,6 +352,41 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
                             int32_t num_q_heads, float scale, float *out, void *workspace,
                             size_t workspace_bytes, void *stream) {
   return run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes, stream, true);
+}
+
+pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new,
+                          pa_dtype src_dtype, void *stream) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set (pa_block_table_set)");
+  const bool fp8 = pool->kv_dtype == PA_DTYPE_FP8_E4M3;
+  if (fp8 ? (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_BF16)
+          : src_dtype != pool->kv_dtype)
+    return fail(PA_ERR_DTYPE, "new K/V dtype %d cannot be written to a pool of dtype %d",
+                (int)src_dtype, (int)pool->kv_dtype);
+  if (pool->batch == 0) return ok();
+  if (!k_new || !v_new) return fail(PA_ERR_NULL, "k_new or v_new is NULL");
+  if ((size_t)pool->batch * pool->num_kv_heads >= (size_t(1) << 31))
+    return fail(PA_ERR_SHAPE, "batch * num_kv_heads too large");
+  pa::AppendArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.table = pool->block_table;
+  a.ctx = pool->context_lens;
+  a.num_blocks = pool->num_blocks;
+  a.hkv = pool->num_kv_heads;
+  a.d = pool->head_dim;
+  a.batch = pool->batch;
+  a.max_blocks = pool->max_blocks_per_seq;
+  a.max_ctx = pool->max_context_len;
+  a.kv = kind_of(pool->kv_dtype);
+  a.src = kind_of(src_dtype);
+  const hipError_t e = pa::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "cache-write kernel launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 pa_status pa_decode_set_workgroups(pa_kv_pool *pool, int32_t count) {

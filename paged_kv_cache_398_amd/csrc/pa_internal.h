@@ -41,6 +41,22 @@ struct LaunchArgs {
   int kv;                   // KvKind
 };
 
+// What the cache-write kernel needs: the pools (written), this step's
+// tables, and the new tokens' K/V rows.
+struct AppendArgs {
+  void *k_cache, *v_cache;  // [num_blocks][16][hkv][d]
+  float *k_scale, *v_scale; // [num_blocks][hkv][16] (FP8 only)
+  const void *k_new, *v_new;  // [batch][hkv][d] of src
+  const int32_t *table;     // [batch][max_blocks]
+  const int32_t *ctx;       // [batch]
+  int32_t num_blocks, hkv, d, batch, max_blocks, max_ctx;
+  int kv;                   // KvKind of the pool
+  int src;                  // KvKind of k_new / v_new (KV_F32 or KV_BF16)
+};
+
+// Enqueue the cache-write kernel (grid batch * hkv waves).
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+
 // True when a kernel is built for (kv, head_dim, group size).
 bool kernel_supported(int kv, int d, int group);
 

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -199,3 +199,22 @@ def test_status_strings():
     for s in range(8):
         assert pa.pa_status_str(s)
     assert pa.pa_status_str(99) == "unknown status"
+
+
+def test_append_errors():
+    h = pa.pa_kv_pool_create(64, 16, 2, 128, "bf16", K, V)
+    try:
+        assert _status(pa.pa_cache_append, h, Q, Q, "bf16", 0) == pa.binding.PA_ERR_STATE
+        pa.pa_block_table_set(h, TBL, CTX, 3, 4, 64)
+        assert _status(pa.pa_cache_append, h, Q, Q, "f32", 0) == pa.binding.PA_ERR_DTYPE
+        assert _status(pa.pa_cache_append, h, None, Q, "bf16", 0) == pa.binding.PA_ERR_NULL
+        pa.pa_block_table_set(h, None, None, 0, 1, 0)
+        pa.pa_cache_append(h, None, None, "bf16", 0)  # an empty batch writes nothing
+    finally:
+        pa.pa_kv_pool_destroy(h)
+    h = pa.pa_kv_pool_create(64, 16, 2, 128, "fp8_e4m3", K, V, KS, VS)
+    try:
+        pa.pa_block_table_set(h, TBL, CTX, 3, 4, 64)
+        assert _status(pa.pa_cache_append, h, Q, Q, "fp8_e4m3", 0) == pa.binding.PA_ERR_DTYPE
+    finally:
+        pa.pa_kv_pool_destroy(h)

@@ -1,0 +1,171 @@
+"""GPU parity of the cache write (pa_cache_append) against the CPU oracle.
+
+The written pools must equal the oracle's byte for byte: a copy for f32 and
+bf16 pools; for FP8 pools the same E4M3FN codes and float32 scales (both
+sides take the quantisation decisions in float32, with correctly rounded
+divisions and nearest-even rounding).  Afterwards a decode run over the
+written cache must match the oracle's decode of the oracle's pools.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_398_amd as pa
+from workloads import Inputs, Spec, make_inputs
+from workloads.device import to_device
+
+from gpu_util import TOL, gpu_decode, max_err, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _new_rows(batch, hkv, d, seed, scale=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    k = (rng.standard_normal((batch, hkv, d)) * scale).astype(np.float32)
+    v = (rng.standard_normal((batch, hkv, d)) * scale).astype(np.float32)
+    return k, v
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _run_append(inp, k_rows, v_rows, src):
+    """Append on the GPU; returns the device inputs (pools now written)."""
+    dev = to_device(inp)
+    if src == "bf16":
+        kt = torch.from_numpy(_bf16_bits(k_rows).view(np.int16)).view(torch.bfloat16).cuda()
+        vt = torch.from_numpy(_bf16_bits(v_rows).view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        kt, vt = torch.from_numpy(k_rows).cuda(), torch.from_numpy(v_rows).cuda()
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, inp.spec.kv_dtype, dev.k_scale, dev.v_scale)
+    try:
+        pool.set_block_table(dev.block_table, dev.context_lens, inp.max_context_len)
+        pool.append(kt, vt)
+        torch.cuda.synchronize()
+    finally:
+        pool.close()
+    return dev
+
+
+def _host(t):
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _oracle_append(inp, k_rows, v_rows, src):
+    kv = inp.spec.kv_dtype
+    if kv == "bf16":
+        kn, vn = _bf16_bits(k_rows), _bf16_bits(v_rows)
+    elif kv == "fp8_e4m3" and src == "bf16":  # the rows the GPU sees, widened exactly
+        kn = oracle.bf16_bits_to_f64(_bf16_bits(k_rows)).astype(np.float32)
+        vn = oracle.bf16_bits_to_f64(_bf16_bits(v_rows)).astype(np.float32)
+    else:
+        kn, vn = k_rows, v_rows
+    return oracle.append_new_tokens(inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens,
+                                    kn, vn, kv, inp.k_scale, inp.v_scale)
+
+
+def _same_bytes(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                          np.ascontiguousarray(b).view(np.uint8))
+
+
+CASES = [("f32", "f32"), ("bf16", "bf16"), ("fp8_e4m3", "f32"), ("fp8_e4m3", "bf16")]
+
+
+@pytest.mark.parametrize("kv,src", CASES)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hkv", [1, 2, 8])
+def test_append_matches_oracle_bytes(kv, src, d, hkv):
+    ctx = (1, 15, 16, 17, 0, 100, 31, 32)
+    spec = Spec(name="append", batch=len(ctx), num_q_heads=hkv, num_kv_heads=hkv, head_dim=d,
+                kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", seed=500 + d + hkv,
+                context_lens=ctx)
+    inp = make_inputs(spec, poison=True)
+    k_rows, v_rows = _new_rows(len(ctx), hkv, d, 600 + d + hkv, scale=3.0)
+    k_rows[0, 0, :] = 0.0  # an all-zero row: scale 1, codes 0
+    say(f"[append] kv={kv} src={src} d={d} hkv={hkv}")
+    dev = _run_append(inp, k_rows, v_rows, src)
+    want_k, want_v, want_ks, want_vs = _oracle_append(inp, k_rows, v_rows, src)
+    assert _same_bytes(_host(dev.k_pool), want_k)
+    assert _same_bytes(_host(dev.v_pool), want_v)
+    if kv == "fp8_e4m3":
+        assert _same_bytes(_host(dev.k_scale), want_ks)
+        assert _same_bytes(_host(dev.v_scale), want_vs)
+
+
+def test_append_fp8_ties_and_extremes():
+    """Exact midpoints between E4M3FN codes go to the even code; subnormal
+    results and the +-448 ends are exact; on the GPU as in the oracle."""
+    d, hkv = 128, 2
+    ctx = (1, 2, 3)
+    spec = Spec(name="ties", batch=3, num_q_heads=2, num_kv_heads=hkv, head_dim=d,
+                kv_dtype="fp8_e4m3", q_dtype="bf16", seed=71, context_lens=ctx)
+    inp = make_inputs(spec)
+    table = oracle.E4M3FN_TABLE
+    mids = np.array([(table[c] + table[c + 1]) / 2 for c in range(0x7E)], np.float32)
+    rows = np.zeros((3, hkv, d), np.float32)
+    # absmax 448 in every row so that the scale is exactly 1: x / scale = x
+    rows[:, :, 0] = 448.0
+    rows[0, 0, 1:] = np.resize(mids, d - 1)
+    rows[0, 1, 1:] = -np.resize(mids, d - 1)
+    rows[1, 0, 1:] = np.resize(mids[::-1], d - 1)
+    rows[1, 1, 1:] = np.resize(table[1:8] * 0.75, d - 1)  # between subnormals
+    rows[2, 0, 1:] = np.resize(np.array([2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 448.0, -448.0]),
+                               d - 1)
+    rows[2, 1, 1:] = -rows[2, 0, 1:]
+    dev = _run_append(inp, rows, rows, "f32")
+    want_k, _, want_ks, _ = _oracle_append(inp, rows, rows, "f32")
+    for b, n in enumerate(ctx):  # scale exactly 1: the codes are those of the values
+        assert np.all(want_ks[inp.block_table[b, 0], :, n - 1] == 1.0)
+    assert _same_bytes(_host(dev.k_pool), want_k)
+    assert _same_bytes(_host(dev.k_scale), want_ks)
+
+
+@pytest.mark.parametrize("kv,src", CASES)
+def test_append_then_decode(kv, src):
+    """Write the new tokens, then attend: the GPU decode over the GPU-written
+    cache equals the oracle's decode over the oracle-written cache."""
+    ctx = (1, 17, 300, 0, 64, 65)
+    spec = Spec(name="append-decode", batch=len(ctx), num_q_heads=16, num_kv_heads=4,
+                head_dim=128, kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16",
+                seed=81, context_lens=ctx)
+    inp = make_inputs(spec, poison=True)
+    k_rows, v_rows = _new_rows(len(ctx), 4, 128, 82)
+    say(f"[append] then decode kv={kv} src={src}")
+    dev = _run_append(inp, k_rows, v_rows, src)
+    k2, v2, ks2, vs2 = _oracle_append(inp, k_rows, v_rows, src)
+    after = Inputs(spec=inp.spec, q=inp.q, k_pool=k2, v_pool=v2, k_scale=ks2, v_scale=vs2,
+                   block_table=inp.block_table, context_lens=inp.context_lens, scale=inp.scale,
+                   used_blocks=inp.used_blocks)
+    got = gpu_decode(after, dev=dev)
+    assert max_err(got, oracle_decode(after)) <= TOL[kv]
+
+
+def test_append_full_size_llama_step():
+    """The Llama-3-8B-shaped step: every sequence's new token at position
+    4095 is written as given (sampled sequences checked byte for byte)."""
+    from workloads import NAMED_SPECS
+    inp = make_inputs(NAMED_SPECS["llama3_8b_b32_ctx4k"])
+    s = inp.spec
+    k_rows, v_rows = _new_rows(s.batch, s.num_kv_heads, s.head_dim, 91)
+    say("[append] llama3 full size")
+    dev = _run_append(inp, k_rows, v_rows, "bf16")
+    kp = _host(dev.k_pool)
+    for b in (0, 13, s.batch - 1):
+        t = int(inp.context_lens[b]) - 1
+        p = inp.block_table[b, t // 16]
+        assert np.array_equal(kp[p, t % 16], _bf16_bits(k_rows[b]))
