@@ -27,6 +27,11 @@ from .decode_attention import (  # noqa: F401
     gather_sequence_head,
     paged_decode_attention,
 )
+from .chunk_attention import (  # noqa: F401
+    chunk_positions,
+    paged_chunk_attention,
+    visible_tokens,
+)
 from .kv_size import kv_cache_bytes  # noqa: F401
 from .cache_write import (  # noqa: F401
     E4M3FN_MAX,

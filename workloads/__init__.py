@@ -14,3 +14,9 @@ from .synthetic import (  # noqa: F401
     make_inputs,
     named_spec,
 )
+from .chunks import (  # noqa: F401
+    CHUNK_SPECS,
+    ChunkInputs,
+    chunk_queries,
+    make_chunk_inputs,
+)
