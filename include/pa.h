@@ -168,6 +168,51 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
                           pa_dtype src_dtype, void *stream);
 
 /*
+ * pa_chunk_run -- attention of several new tokens per sequence (a chunk of
+ * a prompt's prefill, or the candidate tokens of speculative verification).
+ *
+ * Chunked prefill cuts a long prompt into chunks run between decode steps
+ * (d7kj.com page, section 五); speculative decoding checks several draft
+ * tokens in one pass (freetools page, section 技术演进的未来方向).  As for a
+ * decode step, the new tokens' K/V are already in the cache: with the
+ * tables set last, sequence b has context_lens[b] cached tokens of which
+ * the last n_b = q_start[b+1] - q_start[b] are new, so its query rows sit at
+ * positions p = context_lens[b] - n_b .. context_lens[b] - 1, and the row at
+ * position p attends to the cached tokens 0..p (causal; the minimal
+ * implementation of the d7kj.com page, section 六, fed one position at a
+ * time, gives the same outputs).  A row whose position would be negative
+ * (n_b > context_lens[b]) gets zeros.
+ * q: device [total_q][num_q_heads][head_dim] bf16, 16-byte aligned; rows
+ *   q_start[b] .. q_start[b+1] - 1 are sequence b's, in position order.
+ * q_start: device int32 [batch + 1], nondecreasing; a sequence whose rows
+ *   fall outside [0, total_q) or number more than max_q_len is skipped (its
+ *   output rows are not written).
+ * max_q_len: host bound of n_b; it sizes the grid.
+ * out: device float32 [total_q][num_q_heads][head_dim].
+ * Only bf16 pools (and bf16 q); head_dim 64 or 128; num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8}.  Both products run in bf16 on the matrix cores with fp32
+ * accumulation; the softmax weights enter the PV product rounded to bf16
+ * (each within a relative 2^-9; the normaliser sums the same rounded
+ * weights).  No workspace; asynchronous on `stream`.
+ * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_DTYPE,
+ *   PA_ERR_UNSUPPORTED (pool not bf16, group size), PA_ERR_SHAPE,
+ *   PA_ERR_HIP.
+ */
+pa_status pa_chunk_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t num_q_heads,
+                       const int32_t *q_start, int32_t total_q, int32_t max_q_len, float scale,
+                       float *out, void *stream);
+
+/*
+ * pa_chunk_tiles -- launch shape of pa_chunk_run (for tests and tuning).
+ * One workgroup takes *rows_per_workgroup query rows (a row is one (query
+ * token, query head) pair of one KV head's group) of one sequence and KV
+ * head; *workgroups_per_head = ceil(max_q_len * G / rows_per_workgroup).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
+ */
+pa_status pa_chunk_tiles(const pa_kv_pool *pool, int32_t num_q_heads, int32_t max_q_len,
+                         int32_t *rows_per_workgroup, int32_t *workgroups_per_head);
+
+/*
  * pa_decode_workspace_bytes -- device scratch a decode run needs.
  *
  * The kernel's workgroups take equal shares of the batch's 16-token blocks

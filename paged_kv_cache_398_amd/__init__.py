@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     pa_block_table_set,
     pa_block_table_validate,
     pa_cache_append,
+    pa_chunk_run,
+    pa_chunk_tiles,
     pa_decode_fp8_run,
     pa_decode_heads_per_workgroup,
     pa_decode_run,
@@ -76,6 +78,17 @@ class PagedKVPool:
         import torch  # only for the dtype of the rows
         src = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(k_new.dtype, self.kv_dtype)
         pa_cache_append(self.handle, k_new, v_new, src, stream)
+
+    def chunk(self, q, q_start, max_q_len, out, scale=None, stream=None):
+        """Attention of several new tokens per sequence: ``q`` [T][Hq][d]
+        bf16 (rows of sequence b are q_start[b] .. q_start[b+1]-1, the last
+        of its cached positions), ``q_start`` device int32 [B+1],
+        ``max_q_len`` host bound of the rows per sequence -> ``out`` float32
+        [T][Hq][d]."""
+        t, hq = q.shape[0], q.shape[1]
+        if scale is None:
+            scale = 1.0 / self.head_dim ** 0.5
+        pa_chunk_run(self.handle, q, "bf16", hq, q_start, t, max_q_len, scale, out, stream)
 
     def workspace_bytes(self, num_q_heads):
         return pa_decode_workspace_bytes(self.handle, num_q_heads)

@@ -30,6 +30,8 @@ SIGNATURES = [
     ("pa_block_table_set", _i32, [_vp, _vp, _vp, _i32, _i32, _i32]),
     ("pa_block_table_validate", _i32, [_vp, _vp]),
     ("pa_cache_append", _i32, [_vp, _vp, _vp, _i32, _vp]),
+    ("pa_chunk_run", _i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _f32, _vp, _vp]),
+    ("pa_chunk_tiles", _i32, [_vp, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("pa_decode_workspace_bytes", _i32, [_vp, _i32, ctypes.POINTER(_sz)]),
     ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
@@ -131,6 +133,20 @@ def pa_block_table_validate(pool, stream=None) -> None:
 def pa_cache_append(pool, k_new, v_new, src_dtype, stream=None) -> None:
     _check(load_library().pa_cache_append(pool, _ptr(k_new), _ptr(v_new), _dtype(src_dtype),
                                           _stream(stream)))
+
+
+def pa_chunk_run(pool, q, q_dtype, num_q_heads, q_start, total_q, max_q_len, scale, out,
+                 stream=None) -> None:
+    _check(load_library().pa_chunk_run(pool, _ptr(q), _dtype(q_dtype), num_q_heads,
+                                       _ptr(q_start), total_q, max_q_len, float(scale),
+                                       _ptr(out), _stream(stream)))
+
+
+def pa_chunk_tiles(pool, num_q_heads, max_q_len) -> tuple:
+    rows, per_head = _i32(), _i32()
+    _check(load_library().pa_chunk_tiles(pool, num_q_heads, max_q_len, ctypes.byref(rows),
+                                         ctypes.byref(per_head)))
+    return rows.value, per_head.value
 
 
 def pa_decode_workspace_bytes(pool, num_q_heads) -> int:

@@ -389,6 +389,71 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
   return ok();
 }
 
+pa_status pa_chunk_tiles(const pa_kv_pool *pool, int32_t num_q_heads, int32_t max_q_len,
+                         int32_t *rows_per_workgroup, int32_t *workgroups_per_head) {
+  if (!pool || !rows_per_workgroup || !workgroups_per_head)
+    return fail(PA_ERR_NULL, "pool or an output is NULL");
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  if (max_q_len < 0) return fail(PA_ERR_SHAPE, "max_q_len %d < 0", max_q_len);
+  const int group = num_q_heads / pool->num_kv_heads;
+  const int nqt = pa::chunk_tiles_per_item(max_q_len, group, pool->head_dim);
+  *rows_per_workgroup = 16 * nqt;
+  *workgroups_per_head = pa::chunk_items_per_head(max_q_len, group, nqt);
+  return ok();
+}
+
+pa_status pa_chunk_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t num_q_heads,
+                       const int32_t *q_start, int32_t total_q, int32_t max_q_len, float scale,
+                       float *out, void *stream) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set (pa_block_table_set)");
+  if (pool->kv_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "chunk attention is built for bf16 pools only");
+  if (q_dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "chunk attention needs bf16 q");
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (!pa::chunk_supported(pool->head_dim, group))
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", group);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
+  if (total_q < 0 || max_q_len < 0)
+    return fail(PA_ERR_SHAPE, "total_q %d and max_q_len %d must be >= 0", total_q, max_q_len);
+  if (pool->batch == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!q || !out || !q_start) return fail(PA_ERR_NULL, "q, out or q_start is NULL");
+  if (!aligned(q, 16)) return fail(PA_ERR_SHAPE, "q must be 16-byte aligned");
+  if (!aligned(out, 4)) return fail(PA_ERR_SHAPE, "out must be 4-byte aligned");
+  const int nqt = pa::chunk_tiles_per_item(max_q_len, group, pool->head_dim);
+  const int tiles = pa::chunk_items_per_head(max_q_len, group, nqt);
+  if ((int64_t)pool->batch * pool->num_kv_heads * tiles > (int64_t)0x7FFFFFFF)
+    return fail(PA_ERR_SHAPE, "too many workgroups (batch * num_kv_heads * tiles)");
+  pa::ChunkArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.q = q;
+  a.table = pool->block_table;
+  a.ctx = pool->context_lens;
+  a.q_start = q_start;
+  a.out = out;
+  a.num_blocks = pool->num_blocks;
+  a.hkv = pool->num_kv_heads;
+  a.hq = num_q_heads;
+  a.d = pool->head_dim;
+  a.batch = pool->batch;
+  a.max_blocks = pool->max_blocks_per_seq;
+  a.max_ctx = pool->max_context_len;
+  a.max_q = max_q_len;
+  a.total_q = total_q;
+  a.nqt = nqt;
+  a.tiles = tiles;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  const hipError_t e = pa::launch_chunk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "chunk kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 pa_status pa_decode_set_workgroups(pa_kv_pool *pool, int32_t count) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
   if (count < 0 || count > kMaxWorkgroups)

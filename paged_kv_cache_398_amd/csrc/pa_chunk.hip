@@ -1,0 +1,411 @@
+// pa_chunk.hip -- gfx950 (CDNA4) kernel for the attention of several new
+// tokens per sequence over the paged KV cache: a chunk of a long prompt's
+// prefill, or the candidate tokens of speculative verification.
+//
+// What is computed: a sequence of ctx cached tokens whose last n are new has
+// query rows at positions p = ctx - n, ..., ctx - 1 (their K/V are in the
+// cache already, as for a decode step, "KV Cache 深度解析:显存黑洞、
+// PagedAttention 与三路省内存方案" sections 五 and 六); the row at position p
+// attends to the cached tokens 0..p and to nothing later:
+//   out[row][h] = softmax_{t <= p}(scale * q[row][h] . K[t][g]) V[t][g],
+// g = h / G, token t read from physical block table[b][t / 16], slot t % 16.
+// A row whose position would be negative attends to nothing and gets zeros.
+//
+// How.  One workgroup per item: (sequence, KV head g, tile of 16 * NQT query
+// rows, a row being one (query token, head of the group) pair).  Its four
+// waves split the item's visible blocks in pairs (wave w takes pairs w,
+// w + 4, ...) and are combined exactly in LDS at the end.  Both products
+// run on the matrix cores (v_mfma_f32_16x16x32_bf16), transposed so that
+// every lane holds one query row throughout:
+//
+//  - S^T = K Q^T per block: A = K (row = token, lane % 16; k = 8 dims,
+//    lane / 16), B = Q^T (column = query row, lane % 16), D/32 products
+//    over the head dimension.  The result gives lane (row c = lane % 16,
+//    q = lane / 16) the scores of tokens 4q .. 4q+3 of the block for row c.
+//  - The online softmax (running max m and sum l per row, as in the
+//    FlashAttention sections of the pages) is lane-local apart from a
+//    4-lane max; the running max is raised only when a pair's maximum
+//    exceeds it by more than kLag (log2 units), so rescaling is rare.
+//  - O^T += V^T P^T over a pair of blocks (32 tokens): B = P^T in bf16,
+//    lane (row c, k = 8 tokens: 4q..4q+3 of each block), which is exactly
+//    the lane's own probabilities; A = V^T, lane (dim row, same 8 tokens).
+//    Each lane loads the V rows 4q..4q+3 of both blocks at dims EV*c ..
+//    EV*c + EV - 1 (whole 16- or 8-byte slices, every row read in full by
+//    16 lanes) and the EV products take element m of each: product m covers
+//    dims EV*rho + m, rho = 0..15.  The accumulator then gives lane (c, q)
+//    dims 4*EV*q .. 4*EV*q + 4*EV - 1 of row c.
+//
+// Probabilities enter the PV product rounded to bf16 (relative error at
+// most 2^-9 each); the normaliser l sums the same rounded values, so the
+// output is a convex combination of V rows whose weights are off by at most
+// a relative 2^-8.  Positions past a row's own, and blocks or table entries
+// outside the pool, contribute exactly nothing: their scores are replaced by
+// -inf and the V rows of slots past the cached tokens by zeros (selects, not
+// products, so NaN garbage there cannot leak).
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kTok = 16;          // tokens per physical block
+constexpr int kCW = 4;            // waves per workgroup
+constexpr int kCThreads = kCW * 64;
+constexpr float kLag = 8.0f;      // lag allowed to the running max (log2 units)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct ChunkCfg {
+  static constexpr int KM = D / 32;   // S^T products per block (32 dims each)
+  static constexpr int EV = D / 16;   // V elements per lane per token row
+  static constexpr int VDW = EV / 2;  // dwords of that slice
+};
+
+// One lane's share of a pair of blocks.
+template <int D>
+struct PairRegs {
+  uint4 k[2][ChunkCfg<D>::KM];           // token lane%16, dims 32m + 8(lane/16) .. +7
+  uint32_t v[2][4][ChunkCfg<D>::VDW];    // tokens 4(lane/16)+j, dims EV*(lane%16) ..
+  int blk;                               // first block of the pair
+  bool ok[2];                            // block ids inside the pool
+};
+
+__device__ __forceinline__ float max4q(float x) {  // over lanes c, c+16, c+32, c+48
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
+}
+
+__device__ __forceinline__ float sum4q(float x) {
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+template <int N>
+__device__ __forceinline__ void load_dwords(const char *p, uint32_t *dst) {
+  if constexpr (N == 4) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+  } else {
+    static_assert(N == 2, "8- or 16-byte slices");
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    dst[0] = x.x; dst[1] = x.y;
+  }
+}
+
+template <int D, int G, int NQT>
+__global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
+  using C = ChunkCfg<D>;
+  constexpr int KM = C::KM, EV = C::EV, VDW = C::VDW;
+  constexpr int ROWS = 16 * NQT;
+  constexpr int OS = D + 4;  // LDS row stride (floats), spreads the banks
+  __shared__ float s_o[kCW][16][OS];
+  __shared__ float s_m[kCW][ROWS], s_l[kCW][ROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, q = lane >> 4;
+
+  // ---- the item: consecutive workgroup indices alternate between the 8
+  // XCDs, so each XCD is given a contiguous run of items (the tiles of one
+  // (sequence, head) share its L2), heaviest tiles (latest rows) first.
+  const long long items = (long long)a.batch * a.hkv * a.tiles;
+  const long long per = items / 8, rem = items % 8;
+  const int xcd = (int)(blockIdx.x % 8);
+  const long long item = xcd * per + min((long long)xcd, rem) + blockIdx.x / 8;
+  const int bg = (int)(item / a.tiles);
+  const int tile = a.tiles - 1 - (int)(item % a.tiles);
+  const int b = bg / a.hkv, g = bg % a.hkv;
+
+  const int n_ctx = min(max(a.ctx[b], 0), a.max_ctx);
+  const int r0 = a.q_start[b], nq = a.q_start[b + 1] - r0;
+  // no rows, or offsets that would leave q/out: nothing to do
+  if (nq <= 0 || nq > a.max_q || r0 < 0 || r0 > a.total_q - nq) return;
+  const int nrows = nq * G;
+  const int row0 = tile * ROWS;
+  if (row0 >= nrows) return;
+  const int last_row = min(row0 + ROWS, nrows) - 1;
+  const int pmax = n_ctx - nq + last_row / G;  // position of the tile's last row
+  const int nblk = pmax >= 0 ? pmax / kTok + 1 : 0;
+  const int npairs = (nblk + 1) / 2;
+
+  // ---- query rows of the tile (B operands of S^T), positions, state
+  bf16x8_t qf[NQT][KM];
+  int prow[NQT];
+  f32x4_t o[NQT][EV];
+  float mrun[NQT], lsum[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int r = row0 + 16 * t + c;
+    const bool v = r < nrows;
+    prow[t] = v ? n_ctx - nq + r / G : -1;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((size_t)(r0 + (v ? r / G : 0)) * a.hq + g * G + (v ? r % G : 0)) * D + 8 * q;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      const uint4 x = v ? *reinterpret_cast<const uint4 *>(qp + 32 * m) : make_uint4(0, 0, 0, 0);
+      qf[t][m] = as_bf16x8(x);
+    }
+    mrun[t] = -__builtin_huge_valf();
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int m = 0; m < EV; ++m) o[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.scale_log2e;
+
+  // ---- lane offsets inside a block (bytes)
+  const uint32_t k_off = (uint32_t)(((c * a.hkv + g) * D + 8 * q) * 2);
+  const uint32_t v_off = (uint32_t)((((4 * q) * a.hkv + g) * D + EV * c) * 2);
+  const uint32_t v_step = (uint32_t)(a.hkv * D * 2);  // one token row
+  const size_t block_bytes = (size_t)kTok * a.hkv * D * 2;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+
+  // loads of a pair are issued unconditionally: an id outside the pool
+  // reads block 0 and is masked in compute
+  auto issue = [&](PairRegs<D> &P, int pair, int id0, int id1) {
+    P.blk = 2 * pair;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int id = hb ? id1 : id0;
+      P.ok[hb] = (unsigned)id < (unsigned)a.num_blocks;
+      const size_t boff = P.ok[hb] ? (size_t)id * block_bytes : 0;
+      const char *kb = kbase + boff, *vb = vbase + boff;
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+        P.k[hb][m] = *reinterpret_cast<const uint4 *>(kb + (k_off + 64 * m));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_dwords<VDW>(vb + (v_off + j * v_step), P.v[hb][j]);
+    }
+  };
+
+  // A operand of O^T product m: element m of the lane's 8 V rows
+  auto v_operand = [&](const PairRegs<D> &P, int m) {
+    uint32_t d4[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int hb = k2 >> 1, j0 = (k2 & 1) * 2;
+      const uint32_t lo = P.v[hb][j0][m >> 1], hi = P.v[hb][j0 + 1][m >> 1];
+      d4[k2] = (m & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    return as_bf16x8(make_uint4(d4[0], d4[1], d4[2], d4[3]));
+  };
+
+  auto compute = [&](PairRegs<D> &P) {
+    // V rows of slots past the cached tokens (or of a block id outside the
+    // pool) may hold anything, NaN included: zero them by select, since a
+    // zero weight times NaN would still be NaN in the product
+    if (!P.ok[0] || !P.ok[1] || (P.blk + 2) * kTok > n_ctx) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool real = P.ok[hb] && (P.blk + hb) * kTok + 4 * q + j < n_ctx;
+#pragma unroll
+          for (int k = 0; k < VDW; ++k) P.v[hb][j][k] = real ? P.v[hb][j][k] : 0u;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      float x[2][4];
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(P.k[hb][m]), qf[t][m], s, 0, 0, 0);
+        const int tok0 = (P.blk + hb) * kTok + 4 * q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool live = P.ok[hb] && tok0 + j <= prow[t];
+          x[hb][j] = live ? s[j] * sl2 : -__builtin_huge_valf();
+          mx = fmaxf(mx, x[hb][j]);
+        }
+      }
+      mx = max4q(mx);
+      const bool raise = mx > mrun[t] + kLag;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mn = raise ? fmaxf(mrun[t], mx) : mrun[t];
+        const float f = raise ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
+        mrun[t] = mn;
+        lsum[t] *= f;
+#pragma unroll
+        for (int m = 0; m < EV; ++m) o[t][m] *= f;
+      }
+      bf16x8_t pw;
+      float ps = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float xv = x[hb][j];
+          const __bf16 pb = (__bf16)(xv == -__builtin_huge_valf() ? 0.f
+                                                                 : __builtin_amdgcn_exp2f(xv - mrun[t]));
+          pw[4 * hb + j] = pb;
+          ps += (float)pb;  // the normaliser sums the rounded weights
+        }
+      lsum[t] += ps;
+#pragma unroll
+      for (int m = 0; m < EV; ++m)
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(P, m), pw, o[t][m], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: the wave's pairs w, w+4, ..., in chunks of 32 pairs
+  // whose 64 table entries are read by one vector load; a two-stage
+  // pipeline keeps the next pair's loads in flight while one is computed.
+  const int npw = npairs > w ? (npairs - w + kCW - 1) / kCW : 0;
+  const int *trow = a.table + (size_t)b * a.max_blocks;
+  for (int i0 = 0; i0 < npw; i0 += 32) {
+    const int cn = min(32, npw - i0);
+    int tv;
+    {
+      const int blk = 2 * (w + kCW * (i0 + (lane >> 1))) + (lane & 1);
+      tv = blk < nblk ? trow[blk] : -1;
+    }
+    auto id_of = [&](int i, int hb) { return __builtin_amdgcn_readlane(tv, 2 * i + hb); };
+    auto pair_of = [&](int i) { return w + kCW * (i0 + i); };
+    PairRegs<D> A, B;
+    issue(A, pair_of(0), id_of(0, 0), id_of(0, 1));
+    int i = 0;
+    for (; i + 2 < cn; i += 2) {
+      issue(B, pair_of(i + 1), id_of(i + 1, 0), id_of(i + 1, 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A);
+      issue(A, pair_of(i + 2), id_of(i + 2, 0), id_of(i + 2, 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B);
+    }
+    if (i + 1 < cn) {
+      issue(B, pair_of(i + 1), id_of(i + 1, 0), id_of(i + 1, 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A);
+      compute(B);
+    } else {
+      compute(A);
+    }
+  }
+
+  // ---- combine the four waves exactly, one 16-row tile at a time
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const float lt = sum4q(lsum[t]);
+    if (q == 0) {
+      s_m[w][16 * t + c] = mrun[t];
+      s_l[w][16 * t + c] = lt;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int v = 0; v < kCW; ++v) M = fmaxf(M, s_m[v][16 * t + c]);
+    const float f = mrun[t] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mrun[t] - M);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < EV; ++m) s_o[w][c][4 * EV * q + EV * j + m] = o[t][m][j] * f;
+    __syncthreads();
+    for (int idx = tid; idx < 16 * (D / 4); idx += kCThreads) {
+      const int cc = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+      const int r = row0 + 16 * t + cc;
+      if (r < nrows) {
+        float Mr = -__builtin_huge_valf();
+#pragma unroll
+        for (int v = 0; v < kCW; ++v) Mr = fmaxf(Mr, s_m[v][16 * t + cc]);
+        float L = 0.f;
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int v = 0; v < kCW; ++v) {
+          const float mv = s_m[v][16 * t + cc];
+          L += mv == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mv - Mr) * s_l[v][16 * t + cc];
+          const float4 x = *reinterpret_cast<const float4 *>(&s_o[v][cc][d4]);
+          A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float *op = a.out + ((size_t)(r0 + r / G) * a.hq + g * G + r % G) * D + d4;
+        op[0] = A.x * inv; op[1] = A.y * inv; op[2] = A.z * inv; op[3] = A.w * inv;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Most 16-row tiles per workgroup without spilling registers: four for
+// head_dim 64, two for 128.
+constexpr int max_tiles(int d) { return d == 64 ? 4 : 2; }
+
+template <int D, int G>
+hipError_t chunk_by_tiles(const ChunkArgs &a, unsigned grid, hipStream_t s) {
+  if (a.nqt == 1) {
+    hipLaunchKernelGGL((chunk_kernel<D, G, 1>), dim3(grid), dim3(kCThreads), 0, s, a);
+  } else if (a.nqt == 2) {
+    hipLaunchKernelGGL((chunk_kernel<D, G, 2>), dim3(grid), dim3(kCThreads), 0, s, a);
+  } else if constexpr (max_tiles(D) >= 4) {
+    if (a.nqt != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((chunk_kernel<D, G, 4>), dim3(grid), dim3(kCThreads), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t chunk_by_group(const ChunkArgs &a, unsigned grid, hipStream_t s) {
+  switch (a.hq / a.hkv) {
+    case 1: return chunk_by_tiles<D, 1>(a, grid, s);
+    case 2: return chunk_by_tiles<D, 2>(a, grid, s);
+    case 4: return chunk_by_tiles<D, 4>(a, grid, s);
+    case 8: return chunk_by_tiles<D, 8>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int chunk_tiles_per_item(int max_q, int group, int d) {
+  const long long rows = (long long)max_q * group;
+  return rows <= 16 ? 1 : (rows <= 256 ? 2 : max_tiles(d));
+}
+
+int chunk_items_per_head(int max_q, int group, int nqt) {
+  const long long rows = (long long)max_q * group;
+  return (int)((rows + 16LL * nqt - 1) / (16LL * nqt));
+}
+
+bool chunk_supported(int d, int group) {
+  return (d == 64 || d == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_chunk(const ChunkArgs &a, hipStream_t s) {
+  const long long items = (long long)a.batch * a.hkv * a.tiles;
+  if (items == 0) return hipSuccess;
+  if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)items;
+  switch (a.d) {
+    case 64: return chunk_by_group<64>(a, grid, s);
+    case 128: return chunk_by_group<128>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -57,6 +57,37 @@ struct AppendArgs {
 // Enqueue the cache-write kernel (grid batch * hkv waves).
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 
+// What the multi-token (chunk) kernel needs.  Query rows are token-major,
+// rows q_start[b] .. q_start[b+1]-1 belonging to sequence b; the work is
+// counted in items (sequence, KV head, tile of 16 * nqt query rows, a row
+// being one (query token, head of the group) pair).
+struct ChunkArgs {
+  const void *k_cache;      // [num_blocks][16][hkv][d] bf16
+  const void *v_cache;
+  const void *q;            // [total_q][hq][d] bf16
+  const int32_t *table;     // [batch][max_blocks]
+  const int32_t *ctx;       // [batch]
+  const int32_t *q_start;   // [batch + 1]
+  float *out;               // [total_q][hq][d]
+  int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx;
+  int32_t max_q;            // host bound on rows per sequence
+  int32_t total_q;          // rows of q and out
+  int32_t nqt;              // 16-row tiles per item (1, 2, or 4 for d = 64)
+  int32_t tiles;            // items per (sequence, KV head)
+  float scale_log2e;        // softmax scale * log2(e)
+};
+
+// Tiles of 16 rows per item for a launch whose sequences have up to max_q
+// new tokens each, and the items per (sequence, KV head).
+int chunk_tiles_per_item(int max_q, int group, int d);
+int chunk_items_per_head(int max_q, int group, int nqt);
+
+// True when the chunk kernel is built for (head_dim, group size).
+bool chunk_supported(int d, int group);
+
+// Enqueue the chunk kernel (one workgroup per item).
+hipError_t launch_chunk(const ChunkArgs &a, hipStream_t stream);
+
 // True when a kernel is built for (kv, head_dim, group size).
 bool kernel_supported(int kv, int d, int group);
 

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -216,5 +216,65 @@ def test_append_errors():
     try:
         pa.pa_block_table_set(h, TBL, CTX, 3, 4, 64)
         assert _status(pa.pa_cache_append, h, Q, Q, "fp8_e4m3", 0) == pa.binding.PA_ERR_DTYPE
+    finally:
+        pa.pa_kv_pool_destroy(h)
+
+
+def test_chunk_errors():
+    E = pa.binding
+    run = pa.pa_chunk_run
+    QS = 0x900000  # fake q_start
+    h = pa.pa_kv_pool_create(64, 16, 2, 128, "bf16", K, V)
+    try:
+        args = dict(q=Q, q_dtype="bf16", num_q_heads=8, q_start=QS, total_q=4, max_q_len=4,
+                    scale=0.1, out=OUT)
+
+        def st(**kw):
+            a = dict(args, **kw)
+            return _status(run, h, a["q"], a["q_dtype"], a["num_q_heads"], a["q_start"],
+                           a["total_q"], a["max_q_len"], a["scale"], a["out"], stream=0)
+
+        assert st() == E.PA_ERR_STATE  # no table yet
+        pa.pa_block_table_set(h, TBL, CTX, 2, 4, 64)
+        assert st(q_dtype="f32") == E.PA_ERR_DTYPE
+        assert st(num_q_heads=7) == E.PA_ERR_SHAPE
+        assert st(num_q_heads=6) == E.PA_ERR_UNSUPPORTED  # group 3
+        assert st(scale=float("inf")) == E.PA_ERR_SHAPE
+        assert st(total_q=-1) == E.PA_ERR_SHAPE
+        assert st(max_q_len=-2) == E.PA_ERR_SHAPE
+        assert st(q=None) == E.PA_ERR_NULL
+        assert st(q_start=None) == E.PA_ERR_NULL
+        assert st(out=None) == E.PA_ERR_NULL
+        assert st(q=Q + 8) == E.PA_ERR_SHAPE
+        assert "16-byte" in pa.pa_last_error()
+        assert st(out=OUT + 2) == E.PA_ERR_SHAPE
+        # nothing to do: no HIP call is made, so these pass without a GPU
+        run(h, Q, "bf16", 8, QS, 0, 4, 0.1, OUT, stream=0)
+        run(h, Q, "bf16", 8, QS, 4, 0, 0.1, OUT, stream=0)
+        run(h, None, "bf16", 8, None, 0, 0, 0.1, None, stream=0)
+    finally:
+        pa.pa_kv_pool_destroy(h)
+    for kv, sc in (("f32", (None, None)), ("fp8_e4m3", (KS, VS))):
+        h = pa.pa_kv_pool_create(64, 16, 2, 128, kv, K, V, *sc)
+        try:
+            pa.pa_block_table_set(h, TBL, CTX, 2, 4, 64)
+            assert _status(run, h, Q, "bf16", 8, QS, 4, 4, 0.1, OUT, stream=0) == E.PA_ERR_UNSUPPORTED
+        finally:
+            pa.pa_kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("d,hq,max_q,rows,per_head", [
+    (128, 8, 4, 16, 1),      # 4 tokens x G 4 = 16 rows: one tile
+    (128, 8, 5, 32, 1),      # 20 rows: two tiles
+    (128, 8, 2048, 32, 256),  # head_dim 128: at most two tiles per workgroup
+    (64, 8, 2048, 64, 128),  # head_dim 64: four
+    (64, 16, 1, 16, 1),      # G 8, one token
+    (128, 2, 100, 32, 4),    # G 1: 100 rows, two tiles -> 4 workgroups per head
+    (128, 8, 0, 16, 0),
+])
+def test_chunk_launch_shape(d, hq, max_q, rows, per_head):
+    h = pa.pa_kv_pool_create(64, 16, 2, d, "bf16", K, V)
+    try:
+        assert pa.pa_chunk_tiles(h, hq, max_q) == (rows, per_head)
     finally:
         pa.pa_kv_pool_destroy(h)

@@ -1,0 +1,216 @@
+"""GPU parity of the multi-token chunk attention (pa_chunk_run) with the oracle.
+
+Tolerance, from the kernel's arithmetic: q and K are bf16, so the products
+in the scores are exact and summed in fp32; the softmax weights enter the PV
+product rounded to bf16 (relative error at most 2^-9 each) and the
+normaliser sums the same rounded weights, so each output element is a convex
+combination of V values whose weights are off by at most a relative 2^-8:
+  |out - ref| <= 2^-8 * sum_t w_t |V_t| + 1e-4
+(the last term covers fp32 accumulation and the hardware exp2).  The bound
+is evaluated with the oracle itself, by running it on |V|.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_398_amd as pa
+from workloads import Spec, chunk_queries, make_chunk_inputs, make_inputs
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _q_dev(ci):
+    return torch.from_numpy(ci.q.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def gpu_chunk(ci, dev=None, extra_rows=0, q_start=None, max_q=None):
+    base = ci.base
+    dev = dev or to_device(base)
+    s = base.spec
+    T = ci.total_rows
+    out = torch.full((T + extra_rows, s.num_q_heads, s.head_dim), float("nan"),
+                     dtype=torch.float32, device="cuda")
+    qs = torch.from_numpy(ci.q_start if q_start is None else q_start).cuda()
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+    try:
+        pool.set_block_table(dev.block_table, dev.context_lens, base.max_context_len)
+        pool.chunk(_q_dev(ci), qs, ci.max_q_len if max_q is None else max_q, out,
+                   scale=float(base.scale))
+        torch.cuda.synchronize()
+    finally:
+        pool.close()
+    return out.cpu().numpy()
+
+
+def oracle_chunk(ci, seqs=None, abs_v=False):
+    b = ci.base
+    v = (b.v_pool & np.uint16(0x7FFF)) if abs_v else b.v_pool
+    return oracle.paged_chunk_attention(ci.q, b.k_pool, v, b.block_table, b.context_lens,
+                                        ci.q_start, b.scale, kv_dtype="bf16", q_dtype="bf16",
+                                        seqs=seqs)
+
+
+def bound_of(ci, seqs=None):
+    return 2.0 ** -8 * oracle_chunk(ci, seqs, abs_v=True) + 1e-4
+
+
+def rows_of(ci, seqs):
+    return np.concatenate([np.arange(ci.q_start[b], ci.q_start[b + 1]) for b in seqs]
+                          + [np.zeros(0, np.int64)]).astype(np.int64)
+
+
+def assert_parity(ci, got, seqs=None):
+    seqs = list(range(ci.base.spec.batch)) if seqs is None else list(seqs)
+    want, bound = oracle_chunk(ci, seqs), bound_of(ci, seqs)
+    r = rows_of(ci, seqs)
+    err = np.abs(got[r] - want[r])
+    assert np.all(np.isfinite(got[r]))
+    bad = err > bound[r]
+    assert not bad.any(), (f"{bad.sum()} elements over the bound; max err {err.max():.3e}, "
+                           f"worst excess {(err - bound[r]).max():.3e}")
+    return float(err.max()) if err.size else 0.0
+
+
+def _spec(name, d, hq, hkv, ctx, seed):
+    return Spec(name=name, batch=len(ctx), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                kv_dtype="bf16", q_dtype="bf16", seed=seed, context_lens=tuple(ctx))
+
+
+GROUPS = [(8, 8), (8, 4), (8, 2), (16, 2)]  # G = 1, 2, 4, 8
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", GROUPS)
+def test_chunk_small_shapes(d, hq, hkv):
+    """Full prefills (n = ctx), chunks after a prefix, single rows, ragged
+    block tails; unused slots and blocks hold NaN."""
+    ctx = (1, 17, 40, 100, 33, 16, 70)
+    nq = (1, 5, 40, 7, 33, 16, 1)
+    base = make_inputs(_spec("chunk-small", d, hq, hkv, ctx, 700 + d + hq + hkv), poison=True)
+    ci = chunk_queries(base, nq, 800 + d + hq)
+    say(f"[chunk] small d={d} hq={hq} hkv={hkv} rows={ci.total_rows}")
+    err = assert_parity(ci, gpu_chunk(ci))
+    say(f"  max err {err:.2e}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nq", [2, 4, 9, 64, 200])
+def test_chunk_tile_shapes(d, nq):
+    """Each rows-per-workgroup choice (16, 32, and 64 for head_dim 64), with
+    a partial last tile."""
+    ctx = (300, 257, nq)
+    base = make_inputs(_spec("chunk-tiles", d, 8, 2, ctx, 900 + d + nq), poison=True)
+    ci = chunk_queries(base, [nq, nq, nq], 950 + nq)
+    say(f"[chunk] tiles d={d} nq={nq}")
+    assert_parity(ci, gpu_chunk(ci))
+
+
+def test_chunk_rows_before_position_zero():
+    """More new rows than cached tokens: the excess rows are zero."""
+    ctx = (5, 0, 20)
+    nq = (9, 3, 20)
+    base = make_inputs(_spec("chunk-neg", 128, 8, 2, ctx, 1001))
+    ci = chunk_queries(base, nq, 1002)
+    got = gpu_chunk(ci)
+    assert np.all(got[0:4] == 0.0) and np.all(got[9:12] == 0.0)
+    assert_parity(ci, got)
+
+
+def test_chunk_skipped_rows_and_canary():
+    """Sequences with no rows, or with row offsets outside [0, total_q), are
+    skipped; rows past total_q are never written."""
+    ctx = (40, 30, 50, 20)
+    nq = (6, 0, 5, 4)
+    base = make_inputs(_spec("chunk-skip", 64, 4, 2, ctx, 1011))
+    ci = chunk_queries(base, nq, 1012)
+    got = gpu_chunk(ci, extra_rows=3)
+    assert np.all(np.isnan(got[ci.total_rows:]))
+    assert_parity(ci, got)
+    # sequence 3's rows running past total_q: skipped, its rows keep their NaN
+    bad = ci.q_start.copy()
+    bad[4] = ci.total_rows + 2
+    got = gpu_chunk(ci, q_start=bad)
+    assert np.all(np.isnan(got[ci.q_start[3]:]))
+    assert_parity(ci, got, seqs=[0, 2])
+    # more rows than max_q_len: skipped as well
+    got = gpu_chunk(ci, max_q=5)
+    assert np.all(np.isnan(got[ci.q_start[0]:ci.q_start[1]]))
+    assert_parity(ci, got, seqs=[2, 3])
+
+
+def test_chunk_is_deterministic():
+    base = make_inputs(_spec("chunk-det", 128, 32, 8, (1000, 513), 1021))
+    ci = chunk_queries(base, [300, 64], 1022)
+    dev = to_device(base)
+    a, b = gpu_chunk(ci, dev=dev), gpu_chunk(ci, dev=dev)
+    assert np.array_equal(a, b, equal_nan=True)
+
+
+def test_chunk_single_rows_match_decode_path():
+    """One row per sequence is a decode step: the chunk kernel agrees with
+    the decode kernel on the same cache and queries (within the chunk
+    bound), and both with the oracle."""
+    base = make_inputs(_spec("chunk-vs-decode", 128, 32, 8, (4096, 100, 1, 777), 1031))
+    ci = chunk_queries(base, [1, 1, 1, 1], 1032)
+    got = gpu_chunk(ci)
+    assert_parity(ci, got)
+    dev = to_device(base)
+    q = _q_dev(ci)
+    out = torch.empty((4, 32, 128), dtype=torch.float32, device="cuda")
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+    try:
+        pool.set_block_table(dev.block_table, dev.context_lens, base.max_context_len)
+        ws_b = pool.workspace_bytes(32)
+        ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device="cuda")
+        pool.decode(q, out, ws if ws_b else None, scale=float(base.scale))
+        torch.cuda.synchronize()
+    finally:
+        pool.close()
+    bound = bound_of(ci)
+    assert np.all(np.abs(out.cpu().numpy() - got) <= bound + 2e-3)
+
+
+def test_chunk_spec_verify_full_size():
+    """The speculative-verification workload as the benchmark runs it: every
+    row checked."""
+    ci = make_chunk_inputs("spec_verify_b32_ctx4k")
+    say(f"[chunk] spec verify full size, rows={ci.total_rows}")
+    err = assert_parity(ci, gpu_chunk(ci))
+    say(f"  max err {err:.2e}")
+
+
+def test_chunk_prefill_full_size_sampled():
+    """The 2048-row prefill chunk as the benchmark runs it; the oracle
+    computes sampled rows (a row at position p is the one-row chunk of a
+    sequence cut at p + 1 tokens)."""
+    ci = make_chunk_inputs("prefill_chunk2k_b2_ctx4k")
+    base = ci.base
+    say(f"[chunk] prefill full size, rows={ci.total_rows}")
+    got = gpu_chunk(ci)
+    assert np.all(np.isfinite(got))
+    for b in range(base.spec.batch):
+        n, ctx = int(ci.q_lens[b]), int(base.context_lens[b])
+        for i in (0, 1, 15, 16, 17, 255, 1024, n - 2, n - 1):
+            r = int(ci.q_start[b]) + i
+            p = ctx - n + i
+            one = chunk_queries(base, [0] * base.spec.batch, 0)
+            one.q = ci.q[r:r + 1]
+            one.q_start = np.array([0] * (b + 1) + [1] * (base.spec.batch - b), np.int32)
+            one.q_lens = np.diff(one.q_start)
+            cut = base.context_lens.copy()
+            cut[b] = p + 1
+            one.base = type(base)(**{**base.__dict__, "context_lens": cut})
+            want = oracle_chunk(one, seqs=[b])[0]
+            bound = bound_of(one, seqs=[b])[0]
+            err = np.abs(got[r] - want)
+            assert np.all(err <= bound), (b, i, float(err.max()))

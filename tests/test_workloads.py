@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import BLOCK_SIZE, NAMED_SPECS, Spec, make_inputs, named_spec
+from workloads import (BLOCK_SIZE, CHUNK_SPECS, NAMED_SPECS, Spec, make_chunk_inputs, make_inputs,
+                       named_spec)
 
 
 def test_deterministic():
@@ -105,3 +106,16 @@ def test_fp8_scales_are_absmax_over_448():
     deq = vals * sc[..., None]
     err = np.abs(deq - f.k_pool)
     assert np.all(err <= np.abs(f.k_pool) / 16 + sc[..., None] * 2.0 ** -10)
+
+
+@pytest.mark.parametrize("name", sorted(CHUNK_SPECS))
+def test_named_chunk_workloads(name):
+    """Each chunk workload builds; its rows are the last positions of every
+    sequence, in sequence order, and the rows are seeded."""
+    ci = make_chunk_inputs(name)
+    s = ci.base.spec
+    assert ci.q.shape == (ci.total_rows, s.num_q_heads, s.head_dim)
+    assert ci.q_start[0] == 0 and np.all(np.diff(ci.q_start) == ci.q_lens)
+    assert np.all(ci.q_lens <= ci.base.context_lens)
+    again = make_chunk_inputs(name)
+    assert np.array_equal(ci.q, again.q)

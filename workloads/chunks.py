@@ -11,11 +11,11 @@ total rows).  Nothing here computes attention.
 
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 import numpy as np
 
-from .synthetic import Inputs, _to_bf16_bits, make_inputs, named_spec
+from .synthetic import NAMED_SPECS, Inputs, _to_bf16_bits, make_inputs
 
 
 @dataclass
@@ -66,5 +66,5 @@ CHUNK_SPECS = {
 
 def make_chunk_inputs(name: str, poison: bool = False) -> ChunkInputs:
     base_name, over, n, seed = CHUNK_SPECS[name]
-    base = make_inputs(named_spec(base_name, **over), poison=poison)
+    base = make_inputs(replace(NAMED_SPECS[base_name], **over), poison=poison)
     return chunk_queries(base, [n] * base.spec.batch, seed)
