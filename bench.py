@@ -102,6 +102,92 @@ def cpu_baseline(inp, seconds):
     }
 
 
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def chunk_flops(ci):
+    """Algorithmic flops of a chunk: 4 d per (row, query head, visible token)
+    (QK^T and PV, a multiply and an add each)."""
+    import numpy as np
+    s = ci.base.spec
+    tot = 0
+    for b in range(s.batch):
+        n, ctx = int(ci.q_lens[b]), int(ci.base.context_lens[b])
+        tot += int(np.clip(np.arange(ctx - n, ctx) + 1, 0, None).sum())
+    return 4 * s.head_dim * s.num_q_heads * tot
+
+
+def chunk_leg(name, iters, main_inp, main_pools):
+    """Time pa_chunk_run on a named chunk workload: HIP events around every
+    launch (on torch's current stream, the one the launches use)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_398_amd as pa
+    from workloads import CHUNK_SPECS, chunk_queries, make_chunk_inputs
+    from workloads.device import to_device
+
+    base_name, over, n, seed = CHUNK_SPECS[name]
+    own = []
+    if not over and main_inp is not None and main_inp.spec.name == base_name:
+        ci = chunk_queries(main_inp, [n] * main_inp.spec.batch, seed)
+        pools = main_pools  # the decode leg's cycled KV pools, same cache
+    else:
+        ci = make_chunk_inputs(name)
+        dev = to_device(ci.base)
+        p = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+        p.set_block_table(dev.block_table, dev.context_lens, ci.base.max_context_len)
+        own = pools = [p]
+    s = ci.base.spec
+    q = torch.from_numpy(ci.q.view(np.int16)).view(torch.bfloat16).cuda()
+    qs = torch.from_numpy(ci.q_start).cuda()
+    out = torch.empty((ci.total_rows, s.num_q_heads, s.head_dim), dtype=torch.float32,
+                      device="cuda")
+    scale = float(ci.base.scale)
+    for i in range(5):
+        pools[i % len(pools)].chunk(q, qs, ci.max_q_len, out, scale=scale)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        pools[i % len(pools)].chunk(q, qs, ci.max_q_len, out, scale=scale)
+        e1.record()
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError(f"non-finite chunk output ({name})")
+    us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    rows, per_head = pa.pa_chunk_tiles(pools[0].handle, s.num_q_heads, ci.max_q_len)
+    for p in own:
+        p.close()
+    eb = 2
+    nbytes = sum(int(ci.base.context_lens[b]) for b in range(s.batch)) * s.num_kv_heads * \
+        s.head_dim * 2 * eb
+    flops = chunk_flops(ci)
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+    hbm_bound = flops / nbytes < ridge
+    res = {
+        "workload": name, "rows_per_sequence": n, "batch": s.batch,
+        "context_tokens": int(ci.base.max_context_len), "kernel_us": round(us, 2),
+        "kv_bytes": nbytes, "flops": flops, "iters": iters,
+        "rows_per_workgroup": rows, "workgroups": s.batch * s.num_kv_heads * per_head,
+        "pools_cycled": len(pools),
+    }
+    if hbm_bound:
+        a = nbytes / (us * 1e-6) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                           "kernel": "chunk_kernel"}
+    else:
+        a = flops / (us * 1e-6) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": round(a, 1),
+                           "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                           "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "kernel": "chunk_kernel"}
+    log(f"chunk {name}: {us:.1f} us, {res['roofline']['achieved']} "
+        f"{res['roofline']['unit']} ({100 * res['roofline']['frac']:.1f}% of peak)")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +202,8 @@ def main():
                     help="extra steps timed after a 1 GiB cache flush each")
     ap.add_argument("--append-iters", type=int, default=100,
                     help="timed launches of the cache write (0: skip)")
+    ap.add_argument("--chunk-iters", type=int, default=50,
+                    help="timed launches of each multi-token chunk workload (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -231,6 +319,10 @@ def main():
         append = {"us": round(us, 2), "bytes_written": written, "iters": args.append_iters,
                   "note": "pa_cache_append of one new token per sequence, back-to-back launches"}
         log(f"cache write: {us:.2f} us per launch")
+    chunk = None
+    if args.chunk_iters > 0:
+        chunk = [chunk_leg(name, args.chunk_iters, inp, pools)
+                 for name in ("spec_verify_b32_ctx4k", "prefill_chunk2k_b2_ctx4k")]
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -284,6 +376,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "cache_append": append,
+        "chunk": chunk,
     }
     print(json.dumps(res), flush=True)
     for p in pools:
