@@ -32,6 +32,7 @@ from .chunk_attention import (  # noqa: F401
     paged_chunk_attention,
     visible_tokens,
 )
+from .block_manager import BlockManager, OutOfBlocks, block_hash  # noqa: F401
 from .kv_size import kv_cache_bytes  # noqa: F401
 from .cache_write import (  # noqa: F401
     E4M3FN_MAX,
