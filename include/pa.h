@@ -80,7 +80,9 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 4, /* valid but not built: head_dim, group size     */
   PA_ERR_STATE = 5,       /* e.g. run before a block table was set         */
   PA_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned    */
-  PA_ERR_HIP = 7          /* the HIP runtime reported an error             */
+  PA_ERR_HIP = 7,         /* the HIP runtime reported an error             */
+  PA_ERR_NO_BLOCKS = 8,   /* block manager: not enough free or cached blocks */
+  PA_ERR_SEQUENCE = 9     /* block manager: unknown or duplicate sequence id */
 } pa_status;
 
 /*
@@ -201,6 +203,70 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
 pa_status pa_chunk_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t num_q_heads,
                        const int32_t *q_start, int32_t total_q, int32_t max_q_len, float scale,
                        float *out, void *stream);
+
+/*
+ * Block manager (host memory only; no GPU call).
+ *
+ * Hands out the physical blocks of one pool and keeps each sequence's block
+ * table: the PagedAttention memory management of the d7kj.com page,
+ * section 三 (blocks on demand, at most one partly filled block per
+ * sequence, physical blocks shared between sequences) and of the
+ * freetools page's PagedAttention section (blocks released when a request
+ * ends), with the prefix caching of the d7kj.com page, section 五 (blocks
+ * found again by hash), whose hashes chain over every earlier block so that
+ * one different early token defeats reuse (section 七).
+ *   - pa_bm_create: num_blocks >= 1 blocks, ids 0..num_blocks-1 (the pool's);
+ *     prefix_caching != 0 turns the prefix cache on.
+ *   - pa_bm_add: a new sequence (id of the caller's choice) with its prompt.
+ *     *cached_tokens = leading prompt tokens whose K/V already sit in shared
+ *     cached blocks (a multiple of 16, at most n_tokens - 1 rounded down to
+ *     a block): the caller computes and writes only the tokens after them.
+ *   - pa_bm_append: reserve the slot of one more token.  If the sequence's
+ *     last block is shared and not full, it is replaced by a private copy:
+ *     *n_copies = 1 and (copy_src[0], copy_dst[0]) is the copy to perform
+ *     (pa_copy_blocks) before the token is written; else *n_copies = 0.
+ *   - pa_bm_fork: child shares all of parent's blocks (e.g. a beam branch).
+ *   - pa_bm_free: release a sequence's blocks, last block first.
+ *   - pa_bm_table: host int32 table[n][max_blocks] (-1 padded) and lens[n]
+ *     (tokens) of the given sequences, ready for pa_block_table_set once
+ *     copied to the device.
+ *   - pa_bm_stats: free blocks, cached (unreferenced, reusable) blocks and
+ *     live sequences.
+ * Policies: free blocks form a FIFO queue (initially 0..N-1); a registered
+ * full block whose last reference goes stays cached (its K/V still valid)
+ * in a least-recently-released list, and is evicted only when a block is
+ * needed and the free queue is empty.  A full block is registered (16
+ * tokens and a chained FNV-1a hash) when it becomes full, unless a block
+ * with the same content is registered already; lookups compare tokens, so
+ * a hash collision never shares data.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_SEQUENCE (unknown or duplicate
+ *   id), PA_ERR_NO_BLOCKS (not enough free plus cached blocks: the call
+ *   changes nothing).  A manager is not thread-safe.
+ */
+typedef struct pa_block_manager pa_block_manager;
+pa_status pa_bm_create(int32_t num_blocks, int32_t prefix_caching, pa_block_manager **out);
+void pa_bm_destroy(pa_block_manager *bm);
+pa_status pa_bm_add(pa_block_manager *bm, int64_t seq, const int32_t *tokens, int32_t n_tokens,
+                    int32_t *cached_tokens);
+pa_status pa_bm_append(pa_block_manager *bm, int64_t seq, int32_t token, int32_t *copy_src,
+                       int32_t *copy_dst, int32_t *n_copies);
+pa_status pa_bm_fork(pa_block_manager *bm, int64_t parent, int64_t child);
+pa_status pa_bm_free(pa_block_manager *bm, int64_t seq);
+pa_status pa_bm_table(const pa_block_manager *bm, const int64_t *seqs, int32_t n,
+                      int32_t max_blocks, int32_t *table, int32_t *lens);
+pa_status pa_bm_stats(const pa_block_manager *bm, int32_t *free_blocks, int32_t *cached_blocks,
+                      int32_t *sequences);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks of a pool (the copies that
+ * pa_bm_append orders for copy-on-write of a shared block).
+ * pairs: device int32 [n][2] of (src, dst) block ids; the K and V rows of
+ * block src (and its FP8 scales) are copied to block dst.  Pairs naming a
+ * block outside [0, num_blocks), or with src == dst, are skipped.  The dst
+ * blocks must be distinct and none may be another pair's src.
+ * Asynchronous on `stream`.  Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_HIP.
+ */
+pa_status pa_copy_blocks(pa_kv_pool *pool, const int32_t *pairs, int32_t n, void *stream);
 
 /*
  * pa_chunk_tiles -- launch shape of pa_chunk_run (for tests and tuning).

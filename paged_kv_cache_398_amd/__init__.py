@@ -14,7 +14,16 @@ from .binding import (  # noqa: F401
     load_library,
     pa_block_table_set,
     pa_block_table_validate,
+    pa_bm_add,
+    pa_bm_append,
+    pa_bm_create,
+    pa_bm_destroy,
+    pa_bm_fork,
+    pa_bm_free,
+    pa_bm_stats,
+    pa_bm_table,
     pa_cache_append,
+    pa_copy_blocks,
     pa_chunk_run,
     pa_chunk_tiles,
     pa_decode_fp8_run,
@@ -109,6 +118,42 @@ class PagedKVPool:
     def close(self):
         if getattr(self, "handle", None):
             pa_kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class BlockManager:
+    """Owner of one native block manager (host memory; see include/pa.h)."""
+
+    def __init__(self, num_blocks, prefix_caching=True):
+        self.handle = pa_bm_create(num_blocks, prefix_caching)
+
+    def add(self, seq, tokens):
+        return pa_bm_add(self.handle, seq, tokens)
+
+    def append(self, seq, token):
+        return pa_bm_append(self.handle, seq, token)
+
+    def fork(self, parent, child):
+        pa_bm_fork(self.handle, parent, child)
+
+    def free(self, seq):
+        pa_bm_free(self.handle, seq)
+
+    def table(self, seqs, max_blocks):
+        return pa_bm_table(self.handle, seqs, max_blocks)
+
+    def stats(self):
+        return pa_bm_stats(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            pa_bm_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

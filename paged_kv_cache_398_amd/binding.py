@@ -20,9 +20,11 @@ PA_DTYPE = {"f32": 0, "bf16": 1, "fp8_e4m3": 2}
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE = 0, 1, 2, 3
 PA_ERR_UNSUPPORTED, PA_ERR_STATE, PA_ERR_WORKSPACE, PA_ERR_HIP = 4, 5, 6, 7
+PA_ERR_NO_BLOCKS, PA_ERR_SEQUENCE = 8, 9
 
 # (name, restype, argtypes) for every exported symbol of include/pa.h
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_i64, _pi32 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
 SIGNATURES = [
     ("pa_kv_pool_create", _i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(_vp)]),
@@ -32,6 +34,15 @@ SIGNATURES = [
     ("pa_cache_append", _i32, [_vp, _vp, _vp, _i32, _vp]),
     ("pa_chunk_run", _i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _f32, _vp, _vp]),
     ("pa_chunk_tiles", _i32, [_vp, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    ("pa_copy_blocks", _i32, [_vp, _vp, _i32, _vp]),
+    ("pa_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_vp)]),
+    ("pa_bm_destroy", None, [_vp]),
+    ("pa_bm_add", _i32, [_vp, _i64, _vp, _i32, _pi32]),
+    ("pa_bm_append", _i32, [_vp, _i64, _i32, _pi32, _pi32, _pi32]),
+    ("pa_bm_fork", _i32, [_vp, _i64, _i64]),
+    ("pa_bm_free", _i32, [_vp, _i64]),
+    ("pa_bm_table", _i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    ("pa_bm_stats", _i32, [_vp, _pi32, _pi32, _pi32]),
     ("pa_decode_workspace_bytes", _i32, [_vp, _i32, ctypes.POINTER(_sz)]),
     ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
@@ -56,7 +67,8 @@ class PAError(RuntimeError):
 def _name(status: int) -> str:
     return {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE",
             4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_STATE", 6: "PA_ERR_WORKSPACE",
-            7: "PA_ERR_HIP"}.get(status, f"status {status}")
+            7: "PA_ERR_HIP", 8: "PA_ERR_NO_BLOCKS",
+            9: "PA_ERR_SEQUENCE"}.get(status, f"status {status}")
 
 
 _LIB = None
@@ -147,6 +159,68 @@ def pa_chunk_tiles(pool, num_q_heads, max_q_len) -> tuple:
     _check(load_library().pa_chunk_tiles(pool, num_q_heads, max_q_len, ctypes.byref(rows),
                                          ctypes.byref(per_head)))
     return rows.value, per_head.value
+
+
+def pa_copy_blocks(pool, pairs, n, stream=None) -> None:
+    _check(load_library().pa_copy_blocks(pool, _ptr(pairs), n, _stream(stream)))
+
+
+def _host_i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+def pa_bm_create(num_blocks, prefix_caching) -> int:
+    out = _vp()
+    _check(load_library().pa_bm_create(num_blocks, int(bool(prefix_caching)), ctypes.byref(out)))
+    return out.value
+
+
+def pa_bm_destroy(bm) -> None:
+    load_library().pa_bm_destroy(bm)
+
+
+def pa_bm_add(bm, seq, tokens) -> int:
+    arr, p = _host_i32(tokens)
+    cached = _i32()
+    _check(load_library().pa_bm_add(bm, seq, p if arr.size else None, arr.size,
+                                    ctypes.byref(cached)))
+    return cached.value
+
+
+def pa_bm_append(bm, seq, token) -> list:
+    src, dst, n = _i32(), _i32(), _i32()
+    _check(load_library().pa_bm_append(bm, seq, token, ctypes.byref(src), ctypes.byref(dst),
+                                       ctypes.byref(n)))
+    return [(src.value, dst.value)] if n.value else []
+
+
+def pa_bm_fork(bm, parent, child) -> None:
+    _check(load_library().pa_bm_fork(bm, parent, child))
+
+
+def pa_bm_free(bm, seq) -> None:
+    _check(load_library().pa_bm_free(bm, seq))
+
+
+def pa_bm_table(bm, seqs, max_blocks):
+    """-> (int32 [n][max_blocks] numpy table, int32 [n] lengths)."""
+    import numpy as np
+    ids = np.ascontiguousarray(seqs, dtype=np.int64)
+    n = ids.size
+    table = np.empty((n, max_blocks), np.int32)
+    lens = np.empty(n, np.int32)
+    _check(load_library().pa_bm_table(bm, ids.ctypes.data if n else None, n, max_blocks,
+                                      table.ctypes.data if n else None,
+                                      lens.ctypes.data if n else None))
+    return table, lens
+
+
+def pa_bm_stats(bm) -> tuple:
+    f, c, s = _i32(), _i32(), _i32()
+    _check(load_library().pa_bm_stats(bm, ctypes.byref(f), ctypes.byref(c), ctypes.byref(s)))
+    return f.value, c.value, s.value
 
 
 def pa_decode_workspace_bytes(pool, num_q_heads) -> int:

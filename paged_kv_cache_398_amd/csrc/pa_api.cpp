@@ -56,6 +56,18 @@ pa_status ok() {
   return PA_OK;
 }
 
+}  // namespace
+
+namespace pa {
+pa_status record_error(pa_status s, const char *msg) {
+  g_last_error = msg;
+  return s;
+}
+void clear_error() { g_last_error.clear(); }
+}  // namespace pa
+
+namespace {
+
 bool aligned(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 int kind_of(pa_dtype t) {
@@ -389,6 +401,27 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
   return ok();
 }
 
+pa_status pa_copy_blocks(pa_kv_pool *pool, const int32_t *pairs, int32_t n, void *stream) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (n < 0) return fail(PA_ERR_SHAPE, "n %d < 0", n);
+  if (n == 0) return ok();
+  if (!pairs) return fail(PA_ERR_NULL, "pairs is NULL");
+  const int eb = pool->kv_dtype == PA_DTYPE_F32 ? 4 : (pool->kv_dtype == PA_DTYPE_BF16 ? 2 : 1);
+  pa::CopyArgs a{};
+  a.k_cache = pool->k_cache;
+  a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.pairs = pairs;
+  a.n = n;
+  a.num_blocks = pool->num_blocks;
+  a.block_bytes = (int64_t)PA_BLOCK_SIZE * pool->num_kv_heads * pool->head_dim * eb;
+  a.scale_floats = pool->kv_dtype == PA_DTYPE_FP8_E4M3 ? pool->num_kv_heads * PA_BLOCK_SIZE : 0;
+  const hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "block copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 pa_status pa_chunk_tiles(const pa_kv_pool *pool, int32_t num_q_heads, int32_t max_q_len,
                          int32_t *rows_per_workgroup, int32_t *workgroups_per_head) {
   if (!pool || !rows_per_workgroup || !workgroups_per_head)
@@ -534,6 +567,8 @@ const char *pa_status_str(pa_status s) {
     case PA_ERR_STATE: return "bad state";
     case PA_ERR_WORKSPACE: return "bad workspace";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "no free block";
+    case PA_ERR_SEQUENCE: return "unknown or duplicate sequence";
   }
   return "unknown status";
 }

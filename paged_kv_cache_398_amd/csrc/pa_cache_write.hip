@@ -97,7 +97,37 @@ hipError_t append_by_dim(const AppendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One workgroup per (src, dst) pair: the K and V bytes of the block in
+// 16-byte pieces, then the FP8 scales.  Pairs with an id outside the pool,
+// or src == dst, are skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+  const int i = blockIdx.x;
+  const int src = a.pairs[2 * i], dst = a.pairs[2 * i + 1];
+  if ((unsigned)src >= (unsigned)a.num_blocks || (unsigned)dst >= (unsigned)a.num_blocks ||
+      src == dst)
+    return;
+  const int64_t n16 = a.block_bytes / 16;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    char *base = static_cast<char *>(which == 0 ? a.k_cache : a.v_cache);
+    const uint4 *from = reinterpret_cast<const uint4 *>(base + (size_t)src * a.block_bytes);
+    uint4 *to = reinterpret_cast<uint4 *>(base + (size_t)dst * a.block_bytes);
+    for (int64_t k = threadIdx.x; k < n16; k += 256) to[k] = from[k];
+    if (a.scale_floats > 0) {
+      float *sc = which == 0 ? a.k_scale : a.v_scale;
+      for (int k = threadIdx.x; k < a.scale_floats; k += 256)
+        sc[(size_t)dst * a.scale_floats + k] = sc[(size_t)src * a.scale_floats + k];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)a.n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;

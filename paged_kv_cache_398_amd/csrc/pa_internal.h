@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 #ifndef PA_WAVES
 #define PA_WAVES 4
 #endif
@@ -93,6 +95,23 @@ bool kernel_supported(int kv, int d, int group);
 
 // Enqueue the attention kernel (grid nwg workgroups of kWaves waves).
 hipError_t launch_attention(const LaunchArgs &a, hipStream_t stream);
+
+// The text pa_last_error() returns: set with a status, or cleared.
+pa_status record_error(pa_status s, const char *msg);
+void clear_error();
+
+// Enqueue a kernel that copies whole blocks (K, V and, with FP8, their
+// scales): pairs[i] = (src, dst), device int32 [n][2]; pairs naming a block
+// outside [0, num_blocks) or src == dst are skipped.
+struct CopyArgs {
+  void *k_cache, *v_cache;
+  float *k_scale, *v_scale;  // FP8 only, else NULL
+  const int32_t *pairs;
+  int32_t n, num_blocks;
+  int64_t block_bytes;       // K (or V) bytes of one block, a multiple of 16
+  int32_t scale_floats;      // scale floats of one block (hkv * 16), 0 if none
+};
+hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
 
 // Enqueue a kernel that sets n 32-bit words to zero (a kernel rather than a
 // memset, so that a captured graph replays it faithfully).

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 27
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -278,3 +278,19 @@ def test_chunk_launch_shape(d, hq, max_q, rows, per_head):
         assert pa.pa_chunk_tiles(h, hq, max_q) == (rows, per_head)
     finally:
         pa.pa_kv_pool_destroy(h)
+
+
+def test_copy_blocks_errors():
+    h = pa.pa_kv_pool_create(64, 16, 2, 128, "bf16", K, V)
+    try:
+        assert _status(pa.pa_copy_blocks, h, None, 3, stream=0) == pa.binding.PA_ERR_NULL
+        assert _status(pa.pa_copy_blocks, h, 0x900000, -1, stream=0) == pa.binding.PA_ERR_SHAPE
+        pa.pa_copy_blocks(h, None, 0, stream=0)  # nothing to copy: no HIP call
+    finally:
+        pa.pa_kv_pool_destroy(h)
+
+
+def test_status_strings_of_the_block_manager():
+    lib = pa.load_library()
+    assert lib.pa_status_str(8) == b"no free block"
+    assert lib.pa_status_str(9) == b"unknown or duplicate sequence"
