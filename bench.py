@@ -188,6 +188,68 @@ def chunk_leg(name, iters, main_inp, main_pools):
     return res
 
 
+def block_manager_leg(iters):
+    """Host cost of the block manager per operation (through the binding),
+    and the block-copy kernel's bandwidth on a batch of copies."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_398_amd as pa
+
+    rng = np.random.Generator(np.random.PCG64(398200))
+    n_blocks = 65536
+    m = pa.BlockManager(n_blocks, True)
+    prompts = [rng.integers(0, 1000, size=int(n)).tolist() for n in rng.integers(100, 2000, 64)]
+    t0 = time.perf_counter()
+    for i, p in enumerate(prompts):
+        m.add(i, p)
+    t1 = time.perf_counter()
+    n_app = 0
+    for _ in range(iters):
+        for i in range(len(prompts)):
+            m.append(i, 7)
+            n_app += 1
+    t2 = time.perf_counter()
+    for i in range(len(prompts)):
+        m.free(i)
+    t3 = time.perf_counter()
+    m.close()
+    # block copies: 4096 distinct (src, dst) pairs of a bf16 Llama-3-8B-shaped pool
+    hkv, d, n_copy = 8, 128, 4096
+    k = torch.empty((2 * n_copy, 16, hkv, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    pool = pa.PagedKVPool(k, v, "bf16")
+    perm = torch.randperm(2 * n_copy, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    pairs = perm.view(n_copy, 2).contiguous().cuda()
+    for _ in range(3):
+        pa.pa_copy_blocks(pool.handle, pairs, n_copy)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for e0, e1 in evs:
+        e0.record()
+        pa.pa_copy_blocks(pool.handle, pairs, n_copy)
+        e1.record()
+    torch.cuda.synchronize()
+    us = statistics.fmean(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3
+    pool.close()
+    nbytes = n_copy * 16 * hkv * d * 2 * 2 * 2  # K and V, read and written
+    a = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "add_us_per_token": round((t1 - t0) * 1e6 / sum(len(p) for p in prompts), 4),
+        "append_us": round((t2 - t1) * 1e6 / n_app, 3),
+        "free_us_per_sequence": round((t3 - t2) * 1e6 / len(prompts), 2),
+        "note": "host time per operation through the Python binding (ctypes call included)",
+        "copy_blocks": {"pairs": n_copy, "kernel_us": round(us, 2), "bytes": nbytes,
+                        "roofline": {"bound": "hbm", "achieved": round(a, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(a / HBM_PEAK_GBS, 4),
+                                     "kernel": "copy_blocks_kernel"}},
+    }
+    log(f"block manager: append {res['append_us']} us; copy_blocks {us:.1f} us "
+        f"({a:.0f} GB/s)")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +266,8 @@ def main():
                     help="timed launches of the cache write (0: skip)")
     ap.add_argument("--chunk-iters", type=int, default=50,
                     help="timed launches of each multi-token chunk workload (0: skip)")
+    ap.add_argument("--bm-iters", type=int, default=20,
+                    help="append rounds of the block-manager leg (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -323,6 +387,7 @@ def main():
     if args.chunk_iters > 0:
         chunk = [chunk_leg(name, args.chunk_iters, inp, pools)
                  for name in ("spec_verify_b32_ctx4k", "prefill_chunk2k_b2_ctx4k")]
+    block_mgr = block_manager_leg(args.bm_iters) if args.bm_iters > 0 else None
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -377,6 +442,7 @@ def main():
         "cpu_baseline": cpu,
         "cache_append": append,
         "chunk": chunk,
+        "block_manager": block_mgr,
     }
     print(json.dumps(res), flush=True)
     for p in pools:
