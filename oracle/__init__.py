@@ -33,6 +33,7 @@ from .chunk_attention import (  # noqa: F401
     visible_tokens,
 )
 from .block_manager import BlockManager, OutOfBlocks, block_hash  # noqa: F401
+from .kivi import kivi_append, kivi_decode_attention, quantize_block  # noqa: F401
 from .kv_size import kv_cache_bytes  # noqa: F401
 from .cache_write import (  # noqa: F401
     E4M3FN_MAX,
