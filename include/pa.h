@@ -69,7 +69,9 @@ typedef struct pa_kv_pool pa_kv_pool; /* opaque host-side handle */
 typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,      /* IEEE binary32                                  */
   PA_DTYPE_BF16 = 1,     /* upper 16 bits of binary32                      */
-  PA_DTYPE_FP8_E4M3 = 2  /* OCP E4M3FN: bias 7, max 448, NaN = S.1111.111  */
+  PA_DTYPE_FP8_E4M3 = 2, /* OCP E4M3FN: bias 7, max 448, NaN = S.1111.111  */
+  PA_DTYPE_INT8_KIVI = 3, /* 8-bit codes, K per channel / V per token (KIVI) */
+  PA_DTYPE_INT4_KIVI = 4  /* 4-bit codes, two per byte, same grouping        */
 } pa_dtype;
 
 typedef enum pa_status {
@@ -256,6 +258,44 @@ pa_status pa_bm_table(const pa_block_manager *bm, const int64_t *seqs, int32_t n
                       int32_t max_blocks, int32_t *table, int32_t *lens);
 pa_status pa_bm_stats(const pa_block_manager *bm, int32_t *free_blocks, int32_t *cached_blocks,
                       int32_t *sequences);
+
+/*
+ * INT8 / INT4 KV cache quantised the KIVI way (freetools page, section
+ * "KV Cache量化：用精度换空间": Key per channel, Value per token, parameters
+ * from the data, the most recent tokens kept at full precision).
+ *
+ * pa_kv_pool_create_kivi -- describe such a pool (no allocation).
+ *   kv_dtype: PA_DTYPE_INT8_KIVI or PA_DTYPE_INT4_KIVI.
+ *   k_codes, v_codes: device [num_blocks][16][num_kv_heads][head_dim * bits / 8]
+ *     (INT4: channel 2i in the low nibble of byte i, 2i+1 in the high one),
+ *     16-byte aligned; a block holds 16 quantised tokens.
+ *   k_params: device fp16 [num_blocks][num_kv_heads][2][head_dim] -- per
+ *     channel of the block: scale (row 0) and min (row 1); 16-byte aligned.
+ *   v_params: device fp16 [num_blocks][num_kv_heads][16][2] -- per token:
+ *     (scale, min); 4-byte aligned.  value = code * scale + min.
+ *   Errors: PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED.
+ * pa_kivi_residual_set -- the bf16 rows of each sequence's partly filled
+ *   last block: device [batch][16][num_kv_heads][head_dim] (row b belongs to
+ *   sequence b of the tables set last; slot t % 16 holds token t).  Tokens
+ *   of full blocks are read through the table, the last context_lens % 16
+ *   tokens from here.  Errors: PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE.
+ * pa_decode_kivi_run -- one decode step over such a pool: q bf16
+ *   [batch][num_q_heads][head_dim], out float32.  No workspace.  Errors as
+ *   pa_decode_run, plus PA_ERR_STATE without a residual.
+ * pa_cache_append on such a pool takes bf16 rows: the new token goes to its
+ *   residual row; the token that fills a block (t % 16 == 15) has the block
+ *   quantised into block_table[b][t / 16]: per channel over the 16 tokens
+ *   for K, per token over head_dim for V, scale = fp16((max - min) /
+ *   (2^bits - 1)) in float32 (1 if zero), min = fp16(min), code =
+ *   clamp(rint((x - min) / scale), 0, 2^bits - 1) in float32.
+ * pa_copy_blocks copies codes and both parameter arrays.
+ */
+pa_status pa_kv_pool_create_kivi(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                 pa_dtype kv_dtype, void *k_codes, void *v_codes, void *k_params,
+                                 void *v_params, pa_kv_pool **out_pool);
+pa_status pa_kivi_residual_set(pa_kv_pool *pool, void *res_k, void *res_v);
+pa_status pa_decode_kivi_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                             int32_t num_q_heads, float scale, float *out, void *stream);
 
 /*
  * pa_copy_blocks -- copy whole physical blocks of a pool (the copies that

@@ -28,12 +28,15 @@ from .binding import (  # noqa: F401
     pa_chunk_tiles,
     pa_decode_fp8_run,
     pa_decode_heads_per_workgroup,
+    pa_decode_kivi_run,
     pa_decode_run,
     pa_decode_set_heads_per_workgroup,
     pa_decode_set_workgroups,
     pa_decode_workgroups,
     pa_decode_workspace_bytes,
+    pa_kivi_residual_set,
     pa_kv_pool_create,
+    pa_kv_pool_create_kivi,
     pa_kv_pool_destroy,
     pa_last_error,
     pa_profile_enable,
@@ -114,6 +117,51 @@ class PagedKVPool:
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         fn = pa_decode_fp8_run if self.kv_dtype == "fp8_e4m3" else pa_decode_run
         fn(self.handle, q, qd, hq, scale, out, workspace, ws_bytes, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            pa_kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class KiviKVPool:
+    """An INT8 / INT4 pool quantised the KIVI way (see include/pa.h).
+
+    ``k_codes``/``v_codes``: device uint8 [N][16][Hkv][d * bits / 8];
+    ``k_params``: device fp16 [N][Hkv][2][d]; ``v_params``: device fp16
+    [N][Hkv][16][2]; ``bits``: 8 or 4."""
+
+    def __init__(self, k_codes, v_codes, k_params, v_params, bits):
+        n, _, hkv, _ = k_codes.shape
+        d = k_params.shape[-1]
+        self.head_dim, self.bits = d, bits
+        self._keep = [k_codes, v_codes, k_params, v_params]
+        self.handle = pa_kv_pool_create_kivi(n, hkv, d, "int8_kivi" if bits == 8 else "int4_kivi",
+                                             k_codes, v_codes, k_params, v_params)
+
+    def set_block_table(self, block_table, context_lens, max_context_len):
+        b, mb = block_table.shape
+        self._tables = [block_table, context_lens]
+        pa_block_table_set(self.handle, block_table, context_lens, b, mb, max_context_len)
+
+    def set_residual(self, res_k, res_v):
+        """bf16 [B][16][Hkv][d]: each sequence's partly filled last block."""
+        self._res = [res_k, res_v]
+        pa_kivi_residual_set(self.handle, res_k, res_v)
+
+    def append(self, k_new, v_new, stream=None):
+        pa_cache_append(self.handle, k_new, v_new, "bf16", stream)
+
+    def decode(self, q, out, scale=None, stream=None):
+        if scale is None:
+            scale = 1.0 / self.head_dim ** 0.5
+        pa_decode_kivi_run(self.handle, q, "bf16", q.shape[1], scale, out, stream)
 
     def close(self):
         if getattr(self, "handle", None):

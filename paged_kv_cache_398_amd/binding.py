@@ -16,7 +16,7 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
 
 PA_BLOCK_SIZE = 16
-PA_DTYPE = {"f32": 0, "bf16": 1, "fp8_e4m3": 2}
+PA_DTYPE = {"f32": 0, "bf16": 1, "fp8_e4m3": 2, "int8_kivi": 3, "int4_kivi": 4}
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE = 0, 1, 2, 3
 PA_ERR_UNSUPPORTED, PA_ERR_STATE, PA_ERR_WORKSPACE, PA_ERR_HIP = 4, 5, 6, 7
@@ -35,6 +35,10 @@ SIGNATURES = [
     ("pa_chunk_run", _i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _f32, _vp, _vp]),
     ("pa_chunk_tiles", _i32, [_vp, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("pa_copy_blocks", _i32, [_vp, _vp, _i32, _vp]),
+    ("pa_kv_pool_create_kivi", _i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                      ctypes.POINTER(_vp)]),
+    ("pa_kivi_residual_set", _i32, [_vp, _vp, _vp]),
+    ("pa_decode_kivi_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp]),
     ("pa_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_vp)]),
     ("pa_bm_destroy", None, [_vp]),
     ("pa_bm_add", _i32, [_vp, _i64, _vp, _i32, _pi32]),
@@ -159,6 +163,25 @@ def pa_chunk_tiles(pool, num_q_heads, max_q_len) -> tuple:
     _check(load_library().pa_chunk_tiles(pool, num_q_heads, max_q_len, ctypes.byref(rows),
                                          ctypes.byref(per_head)))
     return rows.value, per_head.value
+
+
+def pa_kv_pool_create_kivi(num_blocks, num_kv_heads, head_dim, kv_dtype, k_codes, v_codes,
+                           k_params, v_params) -> int:
+    out = _vp()
+    _check(load_library().pa_kv_pool_create_kivi(num_blocks, num_kv_heads, head_dim,
+                                                 _dtype(kv_dtype), _ptr(k_codes), _ptr(v_codes),
+                                                 _ptr(k_params), _ptr(v_params),
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def pa_kivi_residual_set(pool, res_k, res_v) -> None:
+    _check(load_library().pa_kivi_residual_set(pool, _ptr(res_k), _ptr(res_v)))
+
+
+def pa_decode_kivi_run(pool, q, q_dtype, num_q_heads, scale, out, stream=None) -> None:
+    _check(load_library().pa_decode_kivi_run(pool, _ptr(q), _dtype(q_dtype), num_q_heads,
+                                             float(scale), _ptr(out), _stream(stream)))
 
 
 def pa_copy_blocks(pool, pairs, n, stream=None) -> None:

@@ -14,8 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpa.so")
-SOURCES = ["pa_kernels.hip", "pa_cache_write.hip", "pa_chunk.hip", "pa_api.cpp",
-           "pa_block_manager.cpp"]
+SOURCES = ["pa_kernels.hip", "pa_cache_write.hip", "pa_chunk.hip", "pa_kivi.hip",
+           "pa_api.cpp", "pa_block_manager.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled on purpose: the compiler would

@@ -23,6 +23,10 @@ struct pa_kv_pool {
   pa_dtype kv_dtype = PA_DTYPE_F32;
   void *k_cache = nullptr, *v_cache = nullptr;
   float *k_scale = nullptr, *v_scale = nullptr;
+  // INT8 / INT4 (KIVI) pools: bits, fp16 parameters, and this step's residual
+  int32_t kivi_bits = 0;
+  void *k_par = nullptr, *v_par = nullptr;
+  void *res_k = nullptr, *res_v = nullptr;
   // block tables of the current step
   bool table_set = false;
   const int32_t *block_table = nullptr, *context_lens = nullptr;
@@ -144,6 +148,7 @@ Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
 pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, float scale,
               float *out, void *workspace, size_t ws_bytes, void *stream, bool fp8_entry) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (pool->kivi_bits) return fail(PA_ERR_DTYPE, "an INT8/INT4 pool must be run with pa_decode_kivi_run");
   const bool fp8_pool = pool->kv_dtype == PA_DTYPE_FP8_E4M3;
   if (fp8_entry && !fp8_pool)
     return fail(PA_ERR_DTYPE, "pa_decode_fp8_run needs an FP8 E4M3 pool");
@@ -238,6 +243,30 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   return ok();
 }
 
+pa::KiviArgs kivi_args(const pa_kv_pool *p, const void *q, int32_t hq, float scale, float *out) {
+  pa::KiviArgs a{};
+  a.k_codes = p->k_cache;
+  a.v_codes = p->v_cache;
+  a.k_par = p->k_par;
+  a.v_par = p->v_par;
+  a.res_k = p->res_k;
+  a.res_v = p->res_v;
+  a.q = q;
+  a.table = p->block_table;
+  a.ctx = p->context_lens;
+  a.out = out;
+  a.num_blocks = p->num_blocks;
+  a.hkv = p->num_kv_heads;
+  a.hq = hq;
+  a.d = p->head_dim;
+  a.batch = p->batch;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.max_ctx = p->max_context_len;
+  a.bits = p->kivi_bits;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  return a;
+}
+
 void release_events(pa_kv_pool *p) {
   for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
   p->prof_events.clear();
@@ -255,6 +284,8 @@ pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_
   if (!out_pool) return fail(PA_ERR_NULL, "out_pool is NULL");
   *out_pool = nullptr;
   if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "k_cache or v_cache is NULL");
+  if (kv_dtype == PA_DTYPE_INT8_KIVI || kv_dtype == PA_DTYPE_INT4_KIVI)
+    return fail(PA_ERR_DTYPE, "INT8/INT4 pools are created with pa_kv_pool_create_kivi");
   if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16 && kv_dtype != PA_DTYPE_FP8_E4M3)
     return fail(PA_ERR_DTYPE, "unknown kv dtype %d", (int)kv_dtype);
   const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3;
@@ -370,6 +401,20 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
                           pa_dtype src_dtype, void *stream) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
   if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set (pa_block_table_set)");
+  if (pool->kivi_bits) {
+    if (src_dtype != PA_DTYPE_BF16)
+      return fail(PA_ERR_DTYPE, "an INT8/INT4 pool takes bf16 new rows");
+    if (pool->batch == 0) return ok();
+    if (!k_new || !v_new) return fail(PA_ERR_NULL, "k_new or v_new is NULL");
+    if (!pool->res_k || !pool->res_v)
+      return fail(PA_ERR_STATE, "no residual set (pa_kivi_residual_set)");
+    if (!aligned(k_new, 4) || !aligned(v_new, 4))
+      return fail(PA_ERR_SHAPE, "k_new and v_new must be 4-byte aligned");
+    const pa::KiviArgs a = kivi_args(pool, nullptr, 0, 0.f, nullptr);
+    const hipError_t e = pa::launch_kivi_append(a, k_new, v_new, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "cache-write kernel launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   const bool fp8 = pool->kv_dtype == PA_DTYPE_FP8_E4M3;
   if (fp8 ? (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_BF16)
           : src_dtype != pool->kv_dtype)
@@ -401,6 +446,86 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
   return ok();
 }
 
+pa_status pa_kv_pool_create_kivi(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                 pa_dtype kv_dtype, void *k_codes, void *v_codes, void *k_params,
+                                 void *v_params, pa_kv_pool **out_pool) {
+  if (!out_pool) return fail(PA_ERR_NULL, "out_pool is NULL");
+  *out_pool = nullptr;
+  if (kv_dtype != PA_DTYPE_INT8_KIVI && kv_dtype != PA_DTYPE_INT4_KIVI)
+    return fail(PA_ERR_DTYPE, "kv dtype %d is not INT8 or INT4", (int)kv_dtype);
+  if (!k_codes || !v_codes || !k_params || !v_params)
+    return fail(PA_ERR_NULL, "codes or parameters are NULL");
+  if (num_blocks < 1 || num_kv_heads < 1)
+    return fail(PA_ERR_SHAPE, "num_blocks and num_kv_heads must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if ((int64_t)num_kv_heads * head_dim * 4 * PA_BLOCK_SIZE > (int64_t)1 << 30)
+    return fail(PA_ERR_SHAPE, "num_kv_heads too large");
+  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_params, 16) ||
+      !aligned(v_params, 4))
+    return fail(PA_ERR_SHAPE, "codes and K parameters must be 16-byte aligned, V parameters 4");
+  pa_kv_pool *p = new (std::nothrow) pa_kv_pool();
+  if (!p) return fail(PA_ERR_SHAPE, "out of host memory");
+  p->num_blocks = num_blocks;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  p->kv_dtype = kv_dtype;
+  p->kivi_bits = kv_dtype == PA_DTYPE_INT8_KIVI ? 8 : 4;
+  p->k_cache = k_codes;
+  p->v_cache = v_codes;
+  p->k_par = k_params;
+  p->v_par = v_params;
+  *out_pool = p;
+  return ok();
+}
+
+pa_status pa_kivi_residual_set(pa_kv_pool *pool, void *res_k, void *res_v) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (!pool->kivi_bits) return fail(PA_ERR_DTYPE, "only INT8/INT4 pools have a residual");
+  if ((res_k == nullptr) != (res_v == nullptr))
+    return fail(PA_ERR_NULL, "res_k and res_v must both be set or both be NULL");
+  if (res_k && (!aligned(res_k, 4) || !aligned(res_v, 4)))
+    return fail(PA_ERR_SHAPE, "the residual must be 4-byte aligned");
+  pool->res_k = res_k;
+  pool->res_v = res_v;
+  return ok();
+}
+
+pa_status pa_decode_kivi_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                             int32_t num_q_heads, float scale, float *out, void *stream) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  if (!pool->kivi_bits) return fail(PA_ERR_DTYPE, "pa_decode_kivi_run needs an INT8/INT4 pool");
+  if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set (pa_block_table_set)");
+  if (q_dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "INT8/INT4 decode needs bf16 q");
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", group);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
+  if (pool->batch == 0) return ok();
+  if (!q || !out) return fail(PA_ERR_NULL, "q or out is NULL");
+  if (!pool->res_k) return fail(PA_ERR_STATE, "no residual set (pa_kivi_residual_set)");
+  if ((size_t)pool->batch * pool->num_kv_heads >= (size_t(1) << 31))
+    return fail(PA_ERR_SHAPE, "batch * num_kv_heads too large");
+  const pa::KiviArgs a = kivi_args(pool, q, num_q_heads, scale, out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool prof = pool->prof_capacity > 0 && pool->prof_count < pool->prof_capacity;
+  hipEvent_t *ev = prof ? &pool->prof_events[2 * (size_t)pool->prof_count] : nullptr;
+  if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if ((e = pa::launch_kivi_attention(a, s)) != hipSuccess)
+    return fail(PA_ERR_HIP, "INT8/INT4 attention kernel launch: %s", hipGetErrorString(e));
+  if (prof) {
+    if ((e = hipEventRecord(ev[1], s)) != hipSuccess)
+      return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    ++pool->prof_count;
+  }
+  return ok();
+}
+
 pa_status pa_copy_blocks(pa_kv_pool *pool, const int32_t *pairs, int32_t n, void *stream) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
   if (n < 0) return fail(PA_ERR_SHAPE, "n %d < 0", n);
@@ -410,13 +535,21 @@ pa_status pa_copy_blocks(pa_kv_pool *pool, const int32_t *pairs, int32_t n, void
   pa::CopyArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
-  a.k_scale = pool->k_scale;
-  a.v_scale = pool->v_scale;
   a.pairs = pairs;
   a.n = n;
   a.num_blocks = pool->num_blocks;
   a.block_bytes = (int64_t)PA_BLOCK_SIZE * pool->num_kv_heads * pool->head_dim * eb;
-  a.scale_floats = pool->kv_dtype == PA_DTYPE_FP8_E4M3 ? pool->num_kv_heads * PA_BLOCK_SIZE : 0;
+  if (pool->kv_dtype == PA_DTYPE_FP8_E4M3) {
+    a.k_par = pool->k_scale;
+    a.v_par = pool->v_scale;
+    a.k_par_words = a.v_par_words = pool->num_kv_heads * PA_BLOCK_SIZE;
+  } else if (pool->kivi_bits) {
+    a.block_bytes = (int64_t)PA_BLOCK_SIZE * pool->num_kv_heads * pool->head_dim * pool->kivi_bits / 8;
+    a.k_par = pool->k_par;
+    a.v_par = pool->v_par;
+    a.k_par_words = pool->num_kv_heads * pool->head_dim;  // 2 * d fp16 per head
+    a.v_par_words = pool->num_kv_heads * PA_BLOCK_SIZE;   // (scale, min) per slot
+  }
   const hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "block copy launch: %s", hipGetErrorString(e));
   return ok();

@@ -98,7 +98,7 @@ hipError_t append_by_dim(const AppendArgs &a, hipStream_t s) {
 }
 
 // One workgroup per (src, dst) pair: the K and V bytes of the block in
-// 16-byte pieces, then the FP8 scales.  Pairs with an id outside the pool,
+// 16-byte pieces, then its parameters (FP8 scales, or KIVI scales and mins).  Pairs with an id outside the pool,
 // or src == dst, are skipped.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   const int i = blockIdx.x;
@@ -113,10 +113,11 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
     const uint4 *from = reinterpret_cast<const uint4 *>(base + (size_t)src * a.block_bytes);
     uint4 *to = reinterpret_cast<uint4 *>(base + (size_t)dst * a.block_bytes);
     for (int64_t k = threadIdx.x; k < n16; k += 256) to[k] = from[k];
-    if (a.scale_floats > 0) {
-      float *sc = which == 0 ? a.k_scale : a.v_scale;
-      for (int k = threadIdx.x; k < a.scale_floats; k += 256)
-        sc[(size_t)dst * a.scale_floats + k] = sc[(size_t)src * a.scale_floats + k];
+    const int words = which == 0 ? a.k_par_words : a.v_par_words;
+    if (words > 0) {
+      uint32_t *par = static_cast<uint32_t *>(which == 0 ? a.k_par : a.v_par);
+      for (int k = threadIdx.x; k < words; k += 256)
+        par[(size_t)dst * words + k] = par[(size_t)src * words + k];
     }
   }
 }

@@ -96,6 +96,24 @@ bool kernel_supported(int kv, int d, int group);
 // Enqueue the attention kernel (grid nwg workgroups of kWaves waves).
 hipError_t launch_attention(const LaunchArgs &a, hipStream_t stream);
 
+// An INT8 / INT4 pool quantised the KIVI way (codes, fp16 parameters) with
+// the bf16 residual of each sequence's partly filled last block.
+struct KiviArgs {
+  void *k_codes, *v_codes;  // [num_blocks][16][hkv][d * bits / 8]
+  void *k_par;              // fp16 [num_blocks][hkv][2][d]: scales, then mins
+  void *v_par;              // fp16 [num_blocks][hkv][16][2]: (scale, min) per slot
+  void *res_k, *res_v;      // bf16 [batch][16][hkv][d]
+  const void *q;            // bf16 [batch][hq][d]
+  const int32_t *table;     // [batch][max_blocks]
+  const int32_t *ctx;       // [batch]
+  float *out;               // [batch][hq][d]
+  int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx, bits;
+  float scale_log2e;
+};
+hipError_t launch_kivi_attention(const KiviArgs &a, hipStream_t stream);
+hipError_t launch_kivi_append(const KiviArgs &a, const void *k_new, const void *v_new,
+                              hipStream_t stream);
+
 // The text pa_last_error() returns: set with a status, or cleared.
 pa_status record_error(pa_status s, const char *msg);
 void clear_error();
@@ -105,11 +123,12 @@ void clear_error();
 // outside [0, num_blocks) or src == dst are skipped.
 struct CopyArgs {
   void *k_cache, *v_cache;
-  float *k_scale, *v_scale;  // FP8 only, else NULL
+  void *k_par, *v_par;       // per-block parameters (FP8 scales, KIVI), or NULL
   const int32_t *pairs;
   int32_t n, num_blocks;
   int64_t block_bytes;       // K (or V) bytes of one block, a multiple of 16
-  int32_t scale_floats;      // scale floats of one block (hkv * 16), 0 if none
+  int32_t k_par_words;       // 32-bit words of K parameters per block, 0 if none
+  int32_t v_par_words;       // same for V
 };
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
 

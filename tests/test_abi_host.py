@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 30
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

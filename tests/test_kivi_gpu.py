@@ -1,0 +1,194 @@
+"""GPU parity of the INT8 / INT4 (KIVI-style) KV path with the oracle.
+
+* Decode (pa_decode_kivi_run) against oracle.kivi_decode_attention: all
+  group sizes, head_dim 64 and 128, both widths, lengths with and without a
+  residual (0, 1, 15, 16, 17, ...), table entries past the used blocks
+  poisoned; tolerance 2e-3 (fp32 arithmetic on exact codes and fp16
+  parameters, as for the bf16 path).
+* Cache write (pa_cache_append on such a pool) against oracle.kivi_append:
+  residual rows, codes and fp16 parameters byte for byte, both for tokens
+  that fill their block (quantisation) and for those that do not.
+* From an empty cache, 40 appends and a decode after each, against the
+  oracle fed the same rows.
+* The Llama-3-8B-shaped workload as the benchmark runs it (sampled
+  sequences checked).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_398_amd as pa
+from oracle import kivi
+from workloads import Spec, kivi_state, make_inputs, make_kivi_inputs, named_spec
+
+pytestmark = pytest.mark.gpu
+BLOCK = 16
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.cuda()
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+class Gpu:
+    def __init__(self, kc, vc, kp, vp, rk, rv, bits):
+        self.t = [_dev(x) for x in (kc, vc, kp, vp, rk, rv)]
+        self.pool = pa.KiviKVPool(self.t[0], self.t[1], self.t[2], self.t[3], bits)
+        self.pool.set_residual(self.t[4], self.t[5])
+
+    def tables(self, table, lens, max_ctx):
+        self.tb, self.ln = _dev(np.asarray(table, np.int32)), _dev(np.asarray(lens, np.int32))
+        self.pool.set_block_table(self.tb, self.ln, max_ctx)
+
+    def decode(self, q_bits, hq, scale):
+        out = torch.full((q_bits.shape[0], hq, q_bits.shape[2]), float("nan"), device="cuda")
+        self.pool.decode(_dev(q_bits), out, scale=scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def state(self):
+        res = []
+        for x in self.t:
+            h = x.cpu()
+            res.append(h.view(torch.int16).numpy().view(np.uint16) if h.dtype == torch.bfloat16
+                       else h.numpy())
+        return res
+
+    def close(self):
+        self.pool.close()
+
+
+def _table(rng, lens, N, width):
+    table = np.full((len(lens), width), -1, np.int32)
+    perm = rng.permutation(N)
+    used = 0
+    for b, n in enumerate(lens):
+        for j in range(n // BLOCK):
+            table[b, j] = perm[used]
+            used += 1
+    return table
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+def test_kivi_decode_matches_oracle(bits, d, hq, hkv):
+    rng = np.random.Generator(np.random.PCG64(1000 + bits + d + hq + hkv))
+    lens = [0, 1, 15, 16, 17, 100, 257, 64]
+    N = sum(n // BLOCK for n in lens) + 3
+    kc, vc, kp, vp, rk, rv = kivi_state(rng, N, len(lens), hkv, d, bits)
+    width = max(n // BLOCK for n in lens) + 2
+    table = _table(rng, lens, N, width)
+    q = _bf16_bits(rng.standard_normal((len(lens), hq, d)))
+    scale = np.float32(1 / np.sqrt(d))
+    say(f"[kivi] decode bits={bits} d={d} hq={hq} hkv={hkv}")
+    g = Gpu(kc, vc, kp, vp, rk, rv, bits)
+    try:
+        g.tables(table, lens, max(lens))
+        got = g.decode(q, hq, float(scale))
+    finally:
+        g.close()
+    want = kivi.kivi_decode_attention(q, kc, vc, kp, vp, rk, rv, table, np.array(lens), scale, bits)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - want).max() <= 2e-3
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_kivi_append_matches_oracle_bytes(bits, d):
+    rng = np.random.Generator(np.random.PCG64(2000 + bits + d))
+    hkv = 2
+    lens = [16, 5, 32, 0, 48, 1, 31]  # several fill their block (t % 16 == 15)
+    N = 12
+    state = list(kivi_state(rng, N, len(lens), hkv, d, bits))
+    table = np.full((len(lens), 4), -1, np.int32)
+    perm = rng.permutation(N)
+    k = 0
+    for b, n in enumerate(lens):
+        for j in range((n + BLOCK - 1) // BLOCK):
+            table[b, j] = perm[k]
+            k += 1
+    k_new = _bf16_bits(rng.standard_normal((len(lens), hkv, d)) * 3)
+    v_new = _bf16_bits(rng.standard_normal((len(lens), hkv, d)) * 3)
+    k_new[0, 0, :] = _bf16_bits(np.full(d, 1.5))  # a constant row
+    say(f"[kivi] append bits={bits} d={d}")
+    g = Gpu(*state, bits)
+    try:
+        g.tables(table, lens, max(lens))
+        g.pool.append(_dev(k_new), _dev(v_new))
+        torch.cuda.synchronize()
+        got = g.state()
+    finally:
+        g.close()
+    want = kivi.kivi_append(state, table, np.array(lens), k_new, v_new, bits)
+    names = ["k_codes", "v_codes", "k_params", "v_params", "res_k", "res_v"]
+    for name, a, b in zip(names, got, want):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8)), name
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kivi_append_then_decode_from_empty(bits):
+    rng = np.random.Generator(np.random.PCG64(3000 + bits))
+    hkv, hq, d, steps, B = 2, 8, 128, 40, 3
+    N = 12
+    row = d * bits // 8
+    state = [np.zeros((N, BLOCK, hkv, row), np.uint8), np.zeros((N, BLOCK, hkv, row), np.uint8),
+             np.zeros((N, hkv, 2, d), np.float16), np.zeros((N, hkv, BLOCK, 2), np.float16),
+             np.zeros((B, BLOCK, hkv, d), np.uint16), np.zeros((B, BLOCK, hkv, d), np.uint16)]
+    table = rng.permutation(N)[:B * 3].reshape(B, 3).astype(np.int32)
+    g = Gpu(*state, bits)
+    worst = 0.0
+    try:
+        for n in range(1, steps + 1):
+            lens = np.full(B, n, np.int32)
+            g.tables(table, lens, n)
+            k_new = _bf16_bits(rng.standard_normal((B, hkv, d)))
+            v_new = _bf16_bits(rng.standard_normal((B, hkv, d)))
+            g.pool.append(_dev(k_new), _dev(v_new))
+            state = list(kivi.kivi_append(state, table, lens, k_new, v_new, bits))
+            q = _bf16_bits(rng.standard_normal((B, hq, d)))
+            got = g.decode(q, hq, 0.1)
+            want = kivi.kivi_decode_attention(q, *state, table, lens, 0.1, bits)
+            err = float(np.abs(got - want).max())
+            worst = max(worst, err)
+            assert err <= 2e-3, (n, err)
+        say(f"[kivi] append+decode bits={bits}: max err {worst:.2e}")
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kivi_full_size_llama_step(bits):
+    ki = make_kivi_inputs(named_spec("llama3_8b_b32_ctx4k"), bits, 398300 + bits)
+    base = ki.base
+    s = base.spec
+    say(f"[kivi] full size bits={bits}")
+    g = Gpu(ki.k_codes, ki.v_codes, ki.k_params, ki.v_params, ki.res_k, ki.res_v, bits)
+    try:
+        g.tables(base.block_table, base.context_lens, base.max_context_len)
+        got = g.decode(base.q, s.num_q_heads, float(base.scale))
+    finally:
+        g.close()
+    assert np.all(np.isfinite(got))
+    for b in (0, 17, s.batch - 1):
+        want = kivi.kivi_decode_attention(base.q[b:b + 1], ki.k_codes, ki.v_codes, ki.k_params,
+                                          ki.v_params, ki.res_k[b:b + 1], ki.res_v[b:b + 1],
+                                          base.block_table[b:b + 1], base.context_lens[b:b + 1],
+                                          base.scale, bits)
+        assert np.abs(got[b] - want[0]).max() <= 2e-3

@@ -20,3 +20,4 @@ from .chunks import (  # noqa: F401
     chunk_queries,
     make_chunk_inputs,
 )
+from .kivi import KiviInputs, kivi_state, make_kivi_inputs  # noqa: F401
