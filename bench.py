@@ -188,6 +188,74 @@ def chunk_leg(name, iters, main_inp, main_pools):
     return res
 
 
+def kivi_leg(bits, steps, main_inp, layers):
+    """Decode over the INT8 / INT4 (KIVI-style) pool of the decode workload's
+    shape: same table, lengths and queries, codes and fp16 parameters drawn
+    directly; ``layers`` pools cycled; the library's HIP events around
+    each launch on the first pool."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_398_amd as pa
+    from workloads import kivi_state
+
+    s = main_inp.spec
+    rng = np.random.Generator(np.random.PCG64(398400 + bits))
+    pools, keep = [], []
+    for r in range(layers):
+        kc, vc, kp, vp, rk, rv = kivi_state(rng, main_inp.num_blocks, s.batch, s.num_kv_heads,
+                                            s.head_dim, bits)
+        t = [torch.from_numpy(x).cuda() for x in (kc, vc, kp, vp)]
+        res = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (rk, rv)]
+        p = pa.KiviKVPool(*t, bits)
+        p.set_residual(*res)
+        keep.append((t, res))
+        pools.append(p)
+    tb = torch.from_numpy(main_inp.block_table).cuda()
+    ln = torch.from_numpy(main_inp.context_lens).cuda()
+    for p in pools:
+        p.set_block_table(tb, ln, main_inp.max_context_len)
+    q = torch.from_numpy(main_inp.q.view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    scale = float(main_inp.scale)
+    for i in range(10):
+        pools[i % layers].decode(q, out, scale=scale)
+    torch.cuda.synchronize()
+    n_prof = (steps + layers - 1) // layers
+    pa.pa_profile_enable(pools[0].handle, n_prof)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        pools[i % layers].decode(q, out, scale=scale)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = pa.pa_profile_read(pools[0].handle, n_prof)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite INT8/INT4 output")
+    for p in pools:
+        p.close()
+    # bytes a step must read: codes and parameters of the full blocks, bf16
+    # residual rows of the partial ones
+    hkv, d = s.num_kv_heads, s.head_dim
+    per_block = 2 * 16 * hkv * d * bits // 8 + hkv * 2 * d * 2 + hkv * 16 * 4
+    nbytes = 0
+    for n in main_inp.context_lens.tolist():
+        nbytes += (n // 16) * per_block + (n % 16) * hkv * d * 2 * 2
+    bf16_bytes = int(main_inp.context_lens.astype(np.int64).sum()) * hkv * d * 2 * 2
+    us_step = (t1 - t0) / steps * 1e6
+    kus = statistics.fmean(kern) * 1e3
+    a = nbytes / (kus * 1e-6) / 1e9
+    res = {"bits": bits, "us_per_step": round(us_step, 2), "kernel_us": round(kus, 2),
+           "bytes_per_step": nbytes, "bf16_bytes_of_same_cache": bf16_bytes,
+           "bf16_equivalent_tb_s": round(bf16_bytes / (us_step * 1e-6) / 1e12, 3),
+           "roofline": {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
+                        "kernel": "kivi_attention_kernel"}}
+    log(f"INT{bits} KIVI decode: {us_step:.1f} us/step, kernel {kus:.1f} us "
+        f"({a:.0f} GB/s of its {nbytes / 1e6:.0f} MB; bf16-equivalent "
+        f"{res['bf16_equivalent_tb_s']} TB/s)")
+    return res
+
+
 def block_manager_leg(iters):
     """Host cost of the block manager per operation (through the binding),
     and the block-copy kernel's bandwidth on a batch of copies."""
@@ -266,6 +334,8 @@ def main():
                     help="timed launches of the cache write (0: skip)")
     ap.add_argument("--chunk-iters", type=int, default=50,
                     help="timed launches of each multi-token chunk workload (0: skip)")
+    ap.add_argument("--kivi-steps", type=int, default=200,
+                    help="timed steps of each INT8/INT4 decode leg (0: skip)")
     ap.add_argument("--bm-iters", type=int, default=20,
                     help="append rounds of the block-manager leg (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -388,6 +458,9 @@ def main():
         chunk = [chunk_leg(name, args.chunk_iters, inp, pools)
                  for name in ("spec_verify_b32_ctx4k", "prefill_chunk2k_b2_ctx4k")]
     block_mgr = block_manager_leg(args.bm_iters) if args.bm_iters > 0 else None
+    kivi_res = None
+    if args.kivi_steps > 0 and s.kv_dtype == "bf16":
+        kivi_res = [kivi_leg(bits, args.kivi_steps, inp, min(R, 3)) for bits in (8, 4)]
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18  # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -443,6 +516,7 @@ def main():
         "cache_append": append,
         "chunk": chunk,
         "block_manager": block_mgr,
+        "int_kv": kivi_res,
     }
     print(json.dumps(res), flush=True)
     for p in pools:
