@@ -266,9 +266,10 @@ pa_status pa_bm_stats(const pa_block_manager *bm, int32_t *free_blocks, int32_t 
  *
  * pa_kv_pool_create_kivi -- describe such a pool (no allocation).
  *   kv_dtype: PA_DTYPE_INT8_KIVI or PA_DTYPE_INT4_KIVI.
- *   k_codes, v_codes: device [num_blocks][16][num_kv_heads][head_dim * bits / 8]
- *     (INT4: channel 2i in the low nibble of byte i, 2i+1 in the high one),
- *     16-byte aligned; a block holds 16 quantised tokens.
+ *   k_codes, v_codes: device [num_blocks][num_kv_heads][16][head_dim * bits / 8]
+ *     -- head-major, so one head's 16 rows are contiguous whole cache lines
+ *     at either width (INT4: channel 2i in the low nibble of byte i, 2i+1 in
+ *     the high one), 16-byte aligned; a block holds 16 quantised tokens.
  *   k_params: device fp16 [num_blocks][num_kv_heads][2][head_dim] -- per
  *     channel of the block: scale (row 0) and min (row 1); 16-byte aligned.
  *   v_params: device fp16 [num_blocks][num_kv_heads][16][2] -- per token:

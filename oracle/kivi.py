@@ -26,8 +26,9 @@ Readings where the pages are silent (the GPU path follows the same):
   zero; min = fp16(min).  Codes use the stored parameters:
   code = clamp(rint((x - min) / scale), 0, 2^b - 1) in float32 (IEEE
   division, ties to even).
-* Storage: codes [N][16][Hkv][d] (INT8: one byte per code; INT4: two codes
-  per byte, channel 2i in the low nibble and 2i+1 in the high one); K
+* Storage: codes [N][Hkv][16][d], head-major so that one head's rows are
+  contiguous (INT8: one byte per code; INT4: two codes per byte, channel 2i
+  in the low nibble and 2i+1 in the high one); K
   parameters [N][Hkv][2][d] (scales, then minimums); V parameters
   [N][Hkv][16][2] (scale, min per slot); residual rows [B][16][Hkv][d] bf16
   (slot t % 16 of sequence b's partial block).
@@ -109,8 +110,8 @@ def gather_kivi(k_codes, v_codes, k_par, v_par, res_k, res_v, table_row, b, n, g
         p = int(table_row[j])
         kp = k_par[p, g].astype(np.float64)      # [2][d]
         vp = v_par[p, g].astype(np.float64)      # [16][2]
-        K[BLOCK * j: BLOCK * (j + 1)] = kc_all[p, :, g, :] * kp[0] + kp[1]
-        V[BLOCK * j: BLOCK * (j + 1)] = vc_all[p, :, g, :] * vp[:, :1] + vp[:, 1:]
+        K[BLOCK * j: BLOCK * (j + 1)] = kc_all[p, g] * kp[0] + kp[1]
+        V[BLOCK * j: BLOCK * (j + 1)] = vc_all[p, g] * vp[:, :1] + vp[:, 1:]
     r = n - BLOCK * nf
     if r:
         from .formats import bf16_bits_to_f64
@@ -170,11 +171,11 @@ def kivi_append(state, block_table, context_lens, k_new, v_new, bits: int):
             vrows = bf16_bits_to_f64(rv[b, :, g, :]).astype(np.float32)
             kq, kpar, vq, vpar = quantize_block(krows, vrows, bits)
             if bits == 4:
-                kc[p, :, g, :] = pack_int4(kq)
-                vc[p, :, g, :] = pack_int4(vq)
+                kc[p, g] = pack_int4(kq)
+                vc[p, g] = pack_int4(vq)
             else:
-                kc[p, :, g, :] = kq
-                vc[p, :, g, :] = vq
+                kc[p, g] = kq
+                vc[p, g] = vq
             kp[p, g] = kpar
             vp[p, g] = vpar
     return kc, vc, kp, vp, rk, rv

@@ -133,12 +133,12 @@ class PagedKVPool:
 class KiviKVPool:
     """An INT8 / INT4 pool quantised the KIVI way (see include/pa.h).
 
-    ``k_codes``/``v_codes``: device uint8 [N][16][Hkv][d * bits / 8];
+    ``k_codes``/``v_codes``: device uint8 [N][Hkv][16][d * bits / 8];
     ``k_params``: device fp16 [N][Hkv][2][d]; ``v_params``: device fp16
     [N][Hkv][16][2]; ``bits``: 8 or 4."""
 
     def __init__(self, k_codes, v_codes, k_params, v_params, bits):
-        n, _, hkv, _ = k_codes.shape
+        n, hkv, _, _ = k_codes.shape
         d = k_params.shape[-1]
         self.head_dim, self.bits = d, bits
         self._keep = [k_codes, v_codes, k_params, v_params]

@@ -5,8 +5,9 @@
 // "KV Cache量化：用精度换空间"): K and V stored as 8- or 4-bit integers; Key
 // quantised per channel, Value per token (asymmetric, parameters from the
 // data); the most recent tokens kept at full precision.  Concretely:
-//   - a full block of 16 tokens holds codes [16][Hkv][d] (INT4: two per
-//     byte, even channel in the low nibble); K parameters per (block, head,
+//   - a full block of 16 tokens holds codes [Hkv][16][d] (head-major, so one
+//     head's 16 rows are contiguous whole cache lines at either width; INT4:
+//     two per byte, even channel in the low nibble); K parameters per (block, head,
 //     channel) over the block's tokens, V parameters per (block, head, slot)
 //     over head_dim, both as fp16 (scale, min): value = code * scale + min;
 //   - the tokens of a sequence's partly filled last block stay bf16 in a
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kKThreads) void kivi_attention_kernel(KiviArgs a) {
   uint32_t c_off[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p)
-    c_off[p] = (uint32_t)(((p * TPP + slot) * a.hkv + g) * C::ROWB + sub * C::CB);
+    c_off[p] = (uint32_t)((g * kTokK + p * TPP + slot) * C::ROWB + sub * C::CB);
   const char *kc = static_cast<const char *>(a.k_codes);
   const char *vc = static_cast<const char *>(a.v_codes);
   const uint16_t *kpar = static_cast<const uint16_t *>(a.k_par);  // [N][Hkv][2][D]
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(64) void kivi_append_kernel(KiviArgs a, const void 
   uint8_t *kc = static_cast<uint8_t *>(a.k_codes) + (size_t)phys * kTokK * a.hkv * ROWB;
   uint8_t *vc = static_cast<uint8_t *>(a.v_codes) + (size_t)phys * kTokK * a.hkv * ROWB;
   auto store_pair = [&](uint8_t *base, int s, uint32_t q0, uint32_t q1) {
-    uint8_t *row = base + ((size_t)s * a.hkv + g) * ROWB;
+    uint8_t *row = base + ((size_t)g * kTokK + s) * ROWB;
     if constexpr (BITS == 8) {
       *reinterpret_cast<uint16_t *>(row + c0) = (uint16_t)(q0 | (q1 << 8));
     } else {

@@ -148,7 +148,7 @@ def test_kivi_append_then_decode_from_empty(bits):
     hkv, hq, d, steps, B = 2, 8, 128, 40, 3
     N = 12
     row = d * bits // 8
-    state = [np.zeros((N, BLOCK, hkv, row), np.uint8), np.zeros((N, BLOCK, hkv, row), np.uint8),
+    state = [np.zeros((N, hkv, BLOCK, row), np.uint8), np.zeros((N, hkv, BLOCK, row), np.uint8),
              np.zeros((N, hkv, 2, d), np.float16), np.zeros((N, hkv, BLOCK, 2), np.float16),
              np.zeros((B, BLOCK, hkv, d), np.uint16), np.zeros((B, BLOCK, hkv, d), np.uint16)]
     table = rng.permutation(N)[:B * 3].reshape(B, 3).astype(np.int32)

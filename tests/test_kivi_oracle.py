@@ -39,8 +39,8 @@ def _bf16_bits(x):
 
 def random_state(rng, N, B, hkv, d, bits):
     L = (1 << bits) - 1
-    kc = rng.integers(0, L + 1, size=(N, BLOCK, hkv, d), dtype=np.uint8)
-    vc = rng.integers(0, L + 1, size=(N, BLOCK, hkv, d), dtype=np.uint8)
+    kc = rng.integers(0, L + 1, size=(N, hkv, BLOCK, d), dtype=np.uint8)
+    vc = rng.integers(0, L + 1, size=(N, hkv, BLOCK, d), dtype=np.uint8)
     kp = np.empty((N, hkv, 2, d), np.float16)
     kp[:, :, 0] = (np.abs(rng.standard_normal((N, hkv, d))) * 6 / L + 1e-3).astype(np.float16)
     kp[:, :, 1] = (rng.standard_normal((N, hkv, d)) - 3).astype(np.float16)
@@ -138,9 +138,9 @@ def pin_attention_over_independently_dequantised_pool():
         # extra blocks N..N+B-1 appended to each table
         codes_k = kivi.unpack_int4(kc) if bits == 4 else kc
         codes_v = kivi.unpack_int4(vc) if bits == 4 else vc
-        Kd = codes_k * kp[:, None, :, 0, :].astype(np.float64) + kp[:, None, :, 1, :]
-        Vd = codes_v * vp.transpose(0, 2, 1, 3)[..., 0:1].astype(np.float64) + \
-            vp.transpose(0, 2, 1, 3)[..., 1:2]
+        # codes [N][Hkv][16][d] -> values, then to the pool layout [N][16][Hkv][d]
+        Kd = (codes_k * kp[:, :, 0:1, :].astype(np.float64) + kp[:, :, 1:2, :]).transpose(0, 2, 1, 3)
+        Vd = (codes_v * vp[..., 0:1].astype(np.float64) + vp[..., 1:2]).transpose(0, 2, 1, 3)
         Kx = np.concatenate([Kd, bf16_bits_to_f64(rk)])
         Vx = np.concatenate([Vd, bf16_bits_to_f64(rv)])
         t2 = np.concatenate([table, np.full((B, 1), -1, np.int32)], axis=1)
@@ -157,7 +157,7 @@ def pin_append_then_attend_from_empty():
     rng = _rng(6)
     for bits in (8, 4):
         N, hkv, hq, d, steps = 4, 2, 4, 16, 40
-        kc = np.zeros((N, BLOCK, hkv, d // 2 if bits == 4 else d), np.uint8)
+        kc = np.zeros((N, hkv, BLOCK, d // 2 if bits == 4 else d), np.uint8)
         vc = np.zeros_like(kc)
         kp = np.zeros((N, hkv, 2, d), np.float16)
         vp = np.zeros((N, hkv, BLOCK, 2), np.float16)
@@ -193,7 +193,7 @@ def pin_int8_is_close_to_the_unquantised_cache():
     n, hkv, hq, d = 64, 1, 2, 64
     raw_k = _bf16_bits(rng.standard_normal((n, hkv, d)))
     raw_v = _bf16_bits(rng.standard_normal((n, hkv, d)))
-    state = (np.zeros((4, BLOCK, hkv, d), np.uint8), np.zeros((4, BLOCK, hkv, d), np.uint8),
+    state = (np.zeros((4, hkv, BLOCK, d), np.uint8), np.zeros((4, hkv, BLOCK, d), np.uint8),
              np.zeros((4, hkv, 2, d), np.float16), np.zeros((4, hkv, BLOCK, 2), np.float16),
              np.zeros((1, BLOCK, hkv, d), np.uint16), np.zeros((1, BLOCK, hkv, d), np.uint16))
     table = np.array([[0, 1, 2, 3]], np.int32)

@@ -23,7 +23,7 @@ BLOCK = 16
 class KiviInputs:
     base: Inputs          # table, lengths, q (bf16), scale, spec
     bits: int
-    k_codes: np.ndarray   # uint8 [N][16][Hkv][d * bits / 8]
+    k_codes: np.ndarray   # uint8 [N][Hkv][16][d * bits / 8] (head-major)
     v_codes: np.ndarray
     k_params: np.ndarray  # float16 [N][Hkv][2][d]
     v_params: np.ndarray  # float16 [N][Hkv][16][2]
@@ -37,8 +37,8 @@ def _pack4(c):
 
 def kivi_state(rng, n_blocks, batch, hkv, d, bits):
     L = (1 << bits) - 1
-    kc = rng.integers(0, L + 1, size=(n_blocks, BLOCK, hkv, d), dtype=np.uint8)
-    vc = rng.integers(0, L + 1, size=(n_blocks, BLOCK, hkv, d), dtype=np.uint8)
+    kc = rng.integers(0, L + 1, size=(n_blocks, hkv, BLOCK, d), dtype=np.uint8)
+    vc = rng.integers(0, L + 1, size=(n_blocks, hkv, BLOCK, d), dtype=np.uint8)
     kp = np.empty((n_blocks, hkv, 2, d), np.float16)
     kp[:, :, 0] = (np.abs(rng.standard_normal((n_blocks, hkv, d), dtype=np.float32)) * 6 / L
                    + 1e-3).astype(np.float16)
