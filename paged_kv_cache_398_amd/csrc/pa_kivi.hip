@@ -22,10 +22,9 @@
 // wave whose turn it is; the waves' exact states are combined in LDS.  A
 // lane holds a contiguous run of EPL channels of a token row (LPT lanes per
 // row), so quantised blocks and the residual share one accumulator layout.
-// Dequantisation is folded: with K = code * s + m per channel,
-//   q . k = sum_c (q_c s_c) code_c + sum_c q_c m_c,
-// so per block each lane scales its q by s once and the constant q . m is
-// one reduced dot product per head; with V = code * s_t + m_t per token,
+// K is dequantised per element (k = code * s_c + m_c, one multiply-add with
+// the fp16 parameters as operands) once for the G heads that use it; V's
+// dequantisation is folded: with V = code * s_t + m_t per token,
 //   sum_t p_t v_tc = sum_t (p_t s_t) code_tc + sum_t p_t m_t,
 // the second term being one scalar per head, added at the end.
 
@@ -34,8 +33,20 @@
 namespace pa {
 namespace {
 
+#ifndef KIVI_STAGES
+#define KIVI_STAGES 2  // blocks of a wave in flight at once
+#endif
+static_assert(KIVI_STAGES >= 2, "the pipeline needs two stages or more");
+
+#ifndef KIVI_WAVES
+#define KIVI_WAVES 4  // waves per workgroup
+#endif
+#ifndef KIVI_ACC
+#define KIVI_ACC 64   // most accumulator registers per lane
+#endif
+
 constexpr int kTokK = 16;
-constexpr int kKW = 4;  // waves per workgroup
+constexpr int kKW = KIVI_WAVES;  // waves per workgroup
 constexpr int kKThreads = kKW * 64;
 constexpr float kLagK = 8.0f;
 
@@ -76,13 +87,17 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// Lanes per token row: keep the accumulators (G * D / LPT floats) at 64 or
-// fewer.
-constexpr int kivi_lpt(int d, int g) { return g * d / 4 <= 64 ? 4 : (g * d / 8 <= 64 ? 8 : 16); }
+// Lanes per token row: keep the accumulators (G * D / LPT floats) at
+// KIVI_ACC or fewer, and each lane's code slice at one dword or more.
+constexpr int kivi_lpt(int d, int g, int bits) {
+  int l = g * d / 4 <= KIVI_ACC ? 4 : (g * d / 8 <= KIVI_ACC ? 8 : 16);
+  while (l > 4 && (d / l) * bits / 8 < 4) l /= 2;
+  return l;
+}
 
 template <int BITS, int D, int G>
 struct KCfg {
-  static constexpr int LPT = kivi_lpt(D, G);
+  static constexpr int LPT = kivi_lpt(D, G, BITS);
   static constexpr int EPL = D / LPT;              // channels per lane
   static constexpr int CB = EPL * BITS / 8;        // code bytes per lane per row
   static constexpr int CDW = CB / 4;               // code dwords per lane per row
@@ -109,13 +124,24 @@ __device__ __forceinline__ void load_dw(const char *p, uint32_t *dst) {
   }
 }
 
-// Element e of a lane's code slice, as a float.
-template <int BITS>
-__device__ __forceinline__ float code_at(const uint32_t *w, int e) {
-  if constexpr (BITS == 8) {
-    return (float)((w[e >> 2] >> (8 * (e & 3))) & 0xFF);
-  } else {
-    return (float)((w[e >> 3] >> (4 * (e & 7))) & 0xF);
+// A lane's code slice (N dwords) as floats.  INT4: the even and odd nibbles
+// of a dword are first spread to bytes (two masks), so every element is one
+// byte-to-float conversion, as for INT8.
+template <int BITS, int N>
+__device__ __forceinline__ void codes_to_float(const uint32_t *w, float *f) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (BITS == 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[4 * i + j] = (float)((w[i] >> (8 * j)) & 0xFF);
+    } else {
+      const uint32_t even = w[i] & 0x0F0F0F0Fu, odd = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[8 * i + 2 * j] = (float)((even >> (8 * j)) & 0xFF);
+        f[8 * i + 2 * j + 1] = (float)((odd >> (8 * j)) & 0xFF);
+      }
+    }
   }
 }
 
@@ -227,40 +253,39 @@ __global__ __launch_bounds__(kKThreads) void kivi_attention_kernel(KiviArgs a) {
   };
 
   auto compute = [&](const KBlock<BITS, D, G> &bk) {
-    float ks[EPL], km[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL / 2; ++i) {
-      ks[2 * i] = half_lo(bk.ks[i]); ks[2 * i + 1] = half_hi(bk.ks[i]);
-      km[2 * i] = half_lo(bk.km[i]); km[2 * i + 1] = half_hi(bk.km[i]);
-    }
     float s[NPASS][G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float qs[EPL], c0 = 0.f;
+    for (int p = 0; p < NPASS; ++p) {
+      // K of the lane's token, dequantised once for the G heads (one
+      // multiply-add per element with the fp16 scale and min as operands)
+      float kf[EPL];
+      codes_to_float<BITS, CDW>(bk.k[p], kf);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        qs[e] = qf[hh][e] * ks[e];
-        c0 = fmaf(qf[hh][e], km[e], c0);
+      for (int i = 0; i < EPL / 2; ++i) {
+        kf[2 * i] = fmaf(kf[2 * i], half_lo(bk.ks[i]), half_lo(bk.km[i]));
+        kf[2 * i + 1] = fmaf(kf[2 * i + 1], half_hi(bk.ks[i]), half_hi(bk.km[i]));
       }
-      const float cst = row_sum<LPT>(c0);  // q . min over the head dimension
 #pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
+      for (int hh = 0; hh < G; ++hh) {
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; e += 2) {
-          d0 = fmaf(qs[e], code_at<BITS>(bk.k[p], e), d0);
-          d1 = fmaf(qs[e + 1], code_at<BITS>(bk.k[p], e + 1), d1);
+          d0 = fmaf(qf[hh][e], kf[e], d0);
+          d1 = fmaf(qf[hh][e + 1], kf[e + 1], d1);
         }
-        const float x = (row_sum<LPT>(d0 + d1) + cst) * sl2;
+        const float x = row_sum<LPT>(d0 + d1) * sl2;
         s[p][hh] = bk.ok ? x : -__builtin_huge_valf();
       }
     }
+    float vf[NPASS][EPL];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) codes_to_float<BITS, CDW>(bk.v[p], vf[p]);
     softmax_update(s, [&](int p, int hh, float pr) {
       const float vs = half_lo(bk.vp[p]), vmn = half_hi(bk.vp[p]);
       const float pw = pr * vs;
       pm[hh] = fmaf(pr, vmn, pm[hh]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pw, code_at<BITS>(bk.v[p], e), acc[hh][e]);
+      for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pw, vf[p][e], acc[hh][e]);
     });
   };
 
@@ -272,24 +297,20 @@ __global__ __launch_bounds__(kKThreads) void kivi_attention_kernel(KiviArgs a) {
     const int cn = min(64, nbw - c0);
     const int tv = c0 + lane < nbw ? trow[(size_t)w + (size_t)kKW * (c0 + lane)] : -1;
     auto id_of = [&](int i) { return __builtin_amdgcn_readlane(tv, min(i, cn - 1)); };
-    KBlock<BITS, D, G> A, B;
-    issue(A, id_of(0));
-    int i = 0;
-    for (; i + 2 < cn; i += 2) {
-      issue(B, id_of(i + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(A);
-      issue(A, id_of(i + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(B);
-    }
-    if (i + 1 < cn) {
-      issue(B, id_of(i + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(A);
-      compute(B);
-    } else {
-      compute(A);
+    // KIVI_STAGES blocks in flight: block i is computed while blocks
+    // i+1 .. i+KIVI_STAGES-1 load.  Past the wave's last block the loads
+    // repeat that block (id_of clamps; it is in the caches by then) and are
+    // not computed, so no load sits behind a branch.
+    KBlock<BITS, D, G> bk[KIVI_STAGES];
+#pragma unroll
+    for (int st = 0; st < KIVI_STAGES - 1; ++st) issue(bk[st], id_of(st));
+    for (int i = 0; i < cn; i += KIVI_STAGES) {
+#pragma unroll
+      for (int st = 0; st < KIVI_STAGES; ++st) {
+        issue(bk[(st + KIVI_STAGES - 1) % KIVI_STAGES], id_of(i + st + KIVI_STAGES - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + st < cn) compute(bk[st]);
+      }
     }
   }
 
