@@ -222,6 +222,11 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
           for (int k = 0; k < VDW; ++k) P.v[hb][j][k] = real ? P.v[hb][j][k] : 0u;
         }
     }
+    // the A operands of O^T (V^T, one per product m) depend on the pair
+    // only: built once for the NQT tiles
+    bf16x8_t va[EV];
+#pragma unroll
+    for (int m = 0; m < EV; ++m) va[m] = v_operand(P, m);
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
       float x[2][4];
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
       lsum[t] += ps;
 #pragma unroll
       for (int m = 0; m < EV; ++m)
-        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(P, m), pw, o[t][m], 0, 0, 0);
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
     }
   };
 
