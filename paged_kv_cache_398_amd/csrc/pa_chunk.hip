@@ -11,12 +11,19 @@
 // g = h / G, token t read from physical block table[b][t / 16], slot t % 16.
 // A row whose position would be negative attends to nothing and gets zeros.
 //
-// How.  One workgroup per item: (sequence, KV head g, tile of 16 * NQT query
-// rows, a row being one (query token, head of the group) pair).  Its four
-// waves split the item's visible blocks in pairs (wave w takes pairs w,
-// w + 4, ...) and are combined exactly in LDS at the end.  Both products
-// run on the matrix cores (v_mfma_f32_16x16x32_bf16), transposed so that
-// every lane holds one query row throughout:
+// How.  One workgroup per item: (sequence, KV head g, group of query rows,
+// a row being one (query token, head of the group) pair).  Two kernels:
+//
+//  - chunk_kernel, up to 32 rows per item (short chunks, speculative
+//    verification): the four waves split the item's visible blocks in pairs
+//    (wave w takes pairs w, w + 4, ...), loading K/V straight into
+//    registers, and are combined exactly in LDS at the end;
+//  - chunk_wide_kernel, 256 rows per item (long prefill chunks): each wave
+//    owns 64 rows for the whole context, and every pair of blocks is staged
+//    once per workgroup in LDS, from where the four waves read it.
+//
+// In both, the products run on the matrix cores (v_mfma_f32_16x16x32_bf16),
+// transposed so that every lane holds one query row throughout:
 //
 //  - S^T = K Q^T per block: A = K (row = token, lane % 16; k = 8 dims,
 //    lane / 16), B = Q^T (column = query row, lane % 16), D/32 products
@@ -33,7 +40,10 @@
 //    EV*c + EV - 1 (whole 16- or 8-byte slices, every row read in full by
 //    16 lanes) and the EV products take element m of each: product m covers
 //    dims EV*rho + m, rho = 0..15.  The accumulator then gives lane (c, q)
-//    dims 4*EV*q .. 4*EV*q + 4*EV - 1 of row c.
+//    dims 4*EV*q .. 4*EV*q + 4*EV - 1 of row c.  The V^T operands are
+//    built by byte permutes once per pair, shared by the row tiles.
+//  - The row sums l come out of the matrix cores too: one more product per
+//    tile with A = all ones gives every lane the sum of its row's weights.
 //
 // Probabilities enter the PV product rounded to bf16 (relative error at
 // most 2^-9 each); the normaliser l sums the same rounded values, so the
@@ -52,6 +62,9 @@ constexpr int kTok = 16;          // tokens per physical block
 constexpr int kCW = 4;            // waves per workgroup
 constexpr int kCThreads = kCW * 64;
 constexpr float kLag = 8.0f;      // lag allowed to the running max (log2 units)
+// running max before any score: finite, so that exp2(x - m) needs no guard;
+// the first visible score always raises it (anything exceeds it by kLag)
+constexpr float kNoMax = -3.402823466e38f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -72,28 +85,26 @@ struct PairRegs {
   bool ok[2];                            // block ids inside the pool
 };
 
-__device__ __forceinline__ float max4q(float x) {  // over lanes c, c+16, c+32, c+48
+// Maximum over lanes c, c+16, c+32, c+48.  A compare and select: the
+// values are scores or -inf, never NaN, so no quieting of NaN inputs (which
+// fmaxf would add after the lane swaps) is needed.
+__device__ __forceinline__ float max4q(float x) {
   {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const float u = __uint_as_float(r[0]), v = __uint_as_float(r[1]);
+    x = u > v ? u : v;
   }
   {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const float u = __uint_as_float(r[0]), v = __uint_as_float(r[1]);
+    x = u > v ? u : v;
   }
   return x;
 }
 
-__device__ __forceinline__ float sum4q(float x) {
-  {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  return x;
+__device__ __forceinline__ float max8(const float (&x)[2][4]) {
+  return fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+               fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
@@ -150,7 +161,9 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   bf16x8_t qf[NQT][KM];
   int prow[NQT];
   f32x4_t o[NQT][EV];
-  float mrun[NQT], lsum[NQT];
+  f32x4_t l4[NQT];  // row sums of the rounded weights, all four entries equal
+  float mrun[NQT];
+  const float sl2 = a.scale_log2e;
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
     const int r = row0 + 16 * t + c;
@@ -163,12 +176,15 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
       const uint4 x = v ? *reinterpret_cast<const uint4 *>(qp + 32 * m) : make_uint4(0, 0, 0, 0);
       qf[t][m] = as_bf16x8(x);
     }
-    mrun[t] = -__builtin_huge_valf();
-    lsum[t] = 0.f;
+    mrun[t] = kNoMax;
+    l4[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < EV; ++m) o[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const float sl2 = a.scale_log2e;
+  // first position of the tile: a pair ending at or before it is visible to
+  // every row of the item, and needs no mask
+  const int pfirst = n_ctx - nq + row0 / G;
+  const bf16x8_t ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
   // ---- lane offsets inside a block (bytes)
   const uint32_t k_off = (uint32_t)(((c * a.hkv + g) * D + 8 * q) * 2);
@@ -202,25 +218,33 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
       const int hb = k2 >> 1, j0 = (k2 & 1) * 2;
-      const uint32_t lo = P.v[hb][j0][m >> 1], hi = P.v[hb][j0 + 1][m >> 1];
-      d4[k2] = (m & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      // low half from token j0's dword, high half from token j0 + 1's: the
+      // even or odd element of the pair of dims the dwords hold
+      d4[k2] = __builtin_amdgcn_perm(P.v[hb][j0 + 1][m >> 1], P.v[hb][j0][m >> 1],
+                                     (m & 1) ? 0x07060302u : 0x05040100u);
     }
     return as_bf16x8(make_uint4(d4[0], d4[1], d4[2], d4[3]));
   };
 
+  // full: both blocks inside the pool and every token of the pair at or
+  // before the first row's position -- no mask, no zeroed V rows (a
+  // wave-uniform branch; only a row tile's last pairs are not full).
   auto compute = [&](PairRegs<D> &P) {
-    // V rows of slots past the cached tokens (or of a block id outside the
-    // pool) may hold anything, NaN included: zero them by select, since a
-    // zero weight times NaN would still be NaN in the product
-    if (!P.ok[0] || !P.ok[1] || (P.blk + 2) * kTok > n_ctx) {
+    const bool full = P.ok[0] && P.ok[1] && (P.blk + 2) * kTok - 1 <= pfirst;
+    if (!full) {
+      // V rows of slots past the cached tokens (or of a block id outside
+      // the pool) may hold anything, NaN included: zero them by select,
+      // since a zero weight times NaN would still be NaN in the product
+      if (!P.ok[0] || !P.ok[1] || (P.blk + 2) * kTok > n_ctx) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+        for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool real = P.ok[hb] && (P.blk + hb) * kTok + 4 * q + j < n_ctx;
+          for (int j = 0; j < 4; ++j) {
+            const bool real = P.ok[hb] && (P.blk + hb) * kTok + 4 * q + j < n_ctx;
 #pragma unroll
-          for (int k = 0; k < VDW; ++k) P.v[hb][j][k] = real ? P.v[hb][j][k] : 0u;
-        }
+            for (int k = 0; k < VDW; ++k) P.v[hb][j][k] = real ? P.v[hb][j][k] : 0u;
+          }
+      }
     }
     // the A operands of O^T (V^T, one per product m) depend on the pair
     // only: built once for the NQT tiles
@@ -229,51 +253,60 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
     for (int m = 0; m < EV; ++m) va[m] = v_operand(P, m);
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
-      float x[2][4];
-      float mx = -__builtin_huge_valf();
+      f32x4_t s[2];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        s[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < KM; ++m)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(P.k[hb][m]), qf[t][m], s, 0, 0, 0);
-        const int tok0 = (P.blk + hb) * kTok + 4 * q;
+          s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(P.k[hb][m]), qf[t][m], s[hb], 0, 0, 0);
+      }
+      // scaled scores in log2 units.  Their maximum is taken in the block
+      // that forms the products, so its operands are known canonical floats
+      // (no NaN quieting before v_max3); a pair with masked slots takes it
+      // again over the masked values.
+      float x[2][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool live = P.ok[hb] && tok0 + j <= prow[t];
-          x[hb][j] = live ? s[j] * sl2 : -__builtin_huge_valf();
-          mx = fmaxf(mx, x[hb][j]);
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[hb][j] = s[hb][j] * sl2;
+      float mx = max8(x);
+      if (!full) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int tok0 = (P.blk + hb) * kTok + 4 * q;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            x[hb][j] = (P.ok[hb] && tok0 + j <= prow[t]) ? x[hb][j] : -__builtin_huge_valf();
         }
+        mx = max8(x);
       }
       mx = max4q(mx);
       const bool raise = mx > mrun[t] + kLag;
       if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float mn = raise ? fmaxf(mrun[t], mx) : mrun[t];
+        const float mn = raise ? mx : mrun[t];
         const float f = raise ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
         mrun[t] = mn;
-        lsum[t] *= f;
+        l4[t] *= f;
 #pragma unroll
         for (int m = 0; m < EV; ++m) o[t][m] *= f;
       }
+      const float nm = -mrun[t];
       bf16x8_t pw;
-      float ps = 0.f;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float xv = x[hb][j];
-          const __bf16 pb = (__bf16)(xv == -__builtin_huge_valf() ? 0.f
-                                                                 : __builtin_amdgcn_exp2f(xv - mrun[t]));
-          pw[4 * hb + j] = pb;
-          ps += (float)pb;  // the normaliser sums the rounded weights
+          // a masked score (-inf) gives exactly 0
+          pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[hb][j] + nm);
         }
-      lsum[t] += ps;
+      // the normaliser sums the same rounded weights, on the matrix cores
+      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pw, l4[t], 0, 0, 0);
 #pragma unroll
       for (int m = 0; m < EV; ++m)
         o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
     }
   };
-
   // ---- main loop: the wave's pairs w, w+4, ..., in chunks of 32 pairs
   // whose 64 table entries are read by one vector load; a two-stage
   // pipeline keeps the next pair's loads in flight while one is computed.
@@ -312,19 +345,18 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   // ---- combine the four waves exactly, one 16-row tile at a time
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
-    const float lt = sum4q(lsum[t]);
     if (q == 0) {
       s_m[w][16 * t + c] = mrun[t];
-      s_l[w][16 * t + c] = lt;
+      s_l[w][16 * t + c] = l4[t][0];
     }
   }
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
-    float M = -__builtin_huge_valf();
+    float M = kNoMax;
 #pragma unroll
     for (int v = 0; v < kCW; ++v) M = fmaxf(M, s_m[v][16 * t + c]);
-    const float f = mrun[t] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mrun[t] - M);
+    const float f = mrun[t] == kNoMax ? 0.f : __builtin_amdgcn_exp2f(mrun[t] - M);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -334,7 +366,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
       const int cc = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
       const int r = row0 + 16 * t + cc;
       if (r < nrows) {
-        float Mr = -__builtin_huge_valf();
+        float Mr = kNoMax;
 #pragma unroll
         for (int v = 0; v < kCW; ++v) Mr = fmaxf(Mr, s_m[v][16 * t + cc]);
         float L = 0.f;
@@ -342,7 +374,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int v = 0; v < kCW; ++v) {
           const float mv = s_m[v][16 * t + cc];
-          L += mv == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mv - Mr) * s_l[v][16 * t + cc];
+          L += mv == kNoMax ? 0.f : __builtin_amdgcn_exp2f(mv - Mr) * s_l[v][16 * t + cc];
           const float4 x = *reinterpret_cast<const float4 *>(&s_o[v][cc][d4]);
           A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
         }
@@ -355,9 +387,261 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   }
 }
 
-// Most 16-row tiles per workgroup without spilling registers: four for
-// head_dim 64, two for 128.
-constexpr int max_tiles(int d) { return d == 64 ? 4 : 2; }
+// ---------------------------------------------------------------------------
+// Long chunks.  One workgroup per kWideRows query rows of a (sequence, KV
+// head); each wave owns 64 of them (four 16-row tiles) over the whole
+// visible context, so no combine across waves is needed.  Every 32-token
+// pair of blocks is staged once per workgroup in LDS (two stages, one
+// barrier per pair; the next pair's global loads are in flight while the
+// current one is computed) and the four waves read their MFMA operands from
+// there: a K/V byte brought to the CU serves 256 rows, a byte read from LDS
+// serves the wave's 64.  The products, masks and online softmax per 16-row
+// tile are those of chunk_kernel.
+
+constexpr int kWW = 4;                    // waves per workgroup
+constexpr int kWT = 4;                    // 16-row tiles per wave
+constexpr int kWideRows = kWW * kWT * 16; // rows per workgroup
+
+template <int D>
+struct WideCfg {
+  static constexpr int RS = D * 2 + 16;                // LDS row stride (bytes); the 16 B of padding
+                                                       // put the rows read together on distinct banks
+  static constexpr int ROWCH = D / 8;                  // 16-byte chunks per token row
+  static constexpr int NCH = 32 * ROWCH / kCThreads;   // chunks per thread per pair (K, and V)
+  static constexpr int STAGE = 2 * 32 * RS;            // one pair: 32 K rows, then 32 V rows
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
+  using C = ChunkCfg<D>;
+  using WC = WideCfg<D>;
+  constexpr int KM = C::KM, EV = C::EV, VDW = C::VDW;
+  constexpr int RS = WC::RS, NCH = WC::NCH, ROWCH = WC::ROWCH;
+  static_assert(NCH >= 1 && NCH * kCThreads == 32 * ROWCH, "whole chunks per thread");
+  static_assert(kWW * 64 == kCThreads, "one wave per 64 rows");
+  __shared__ __align__(16) char s_kv[2 * WC::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, q = lane >> 4;
+
+  // ---- the item (same numbering as chunk_kernel: a contiguous run per XCD,
+  // latest rows first)
+  const long long items = (long long)a.batch * a.hkv * a.tiles;
+  const long long per = items / 8, rem = items % 8;
+  const int xcd = (int)(blockIdx.x % 8);
+  const long long item = xcd * per + min((long long)xcd, rem) + blockIdx.x / 8;
+  const int bg = (int)(item / a.tiles);
+  const int tile = a.tiles - 1 - (int)(item % a.tiles);
+  const int b = bg / a.hkv, g = bg % a.hkv;
+
+  const int n_ctx = min(max(a.ctx[b], 0), a.max_ctx);
+  const int r0 = a.q_start[b], nq = a.q_start[b + 1] - r0;
+  if (nq <= 0 || nq > a.max_q || r0 < 0 || r0 > a.total_q - nq) return;
+  const int nrows = nq * G;
+  const int row0 = tile * kWideRows;
+  if (row0 >= nrows) return;  // uniform over the workgroup, before any barrier
+  const int last_row = min(row0 + kWideRows, nrows) - 1;
+  const int pmax = n_ctx - nq + last_row / G;
+  const int nblk = pmax >= 0 ? pmax / kTok + 1 : 0;
+  const int npairs = (nblk + 1) / 2;
+
+  // ---- the wave's rows
+  const int wrow0 = row0 + 64 * w;
+  const bool has_rows = wrow0 < nrows;
+  const int pfirst = n_ctx - nq + wrow0 / G;                       // first row's position
+  const int plast = n_ctx - nq + (min(wrow0 + 64, nrows) - 1) / G;  // last row's position
+
+  bf16x8_t qf[kWT][KM];
+  int prow[kWT];
+  f32x4_t o[kWT][EV];
+  f32x4_t l4[kWT];
+  float mrun[kWT];
+#pragma unroll
+  for (int t = 0; t < kWT; ++t) {
+    const int r = wrow0 + 16 * t + c;
+    const bool v = r < nrows;
+    prow[t] = v ? n_ctx - nq + r / G : -1;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((size_t)(r0 + (v ? r / G : 0)) * a.hq + g * G + (v ? r % G : 0)) * D + 8 * q;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      const uint4 x = v ? *reinterpret_cast<const uint4 *>(qp + 32 * m) : make_uint4(0, 0, 0, 0);
+      qf[t][m] = as_bf16x8(x);
+    }
+    mrun[t] = kNoMax;
+    l4[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < EV; ++m) o[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = a.scale_log2e;
+  const bf16x8_t ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+  const int *trow = a.table + (size_t)b * a.max_blocks;
+  const size_t block_bytes = (size_t)kTok * a.hkv * D * 2;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  auto block_id = [&](int blk) { return blk < nblk ? trow[blk] : -1; };
+
+  // ---- staging: thread tid moves chunks tid, tid + 256, ... of the pair's
+  // 32 K rows and 32 V rows (16 chunks of 16 B per row for head_dim 128).
+  // Slots past the cached tokens and blocks outside the pool are stored as
+  // zeros: their scores are masked anyway, and V garbage (NaN) cannot leak
+  // into the products.
+  uint4 sk[NCH], sv[NCH];
+  bool sreal[NCH];
+  auto stage_load = [&](int pair) {
+    const int blk0 = 2 * pair;
+    const int id0 = block_id(blk0), id1 = block_id(blk0 + 1);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + kCThreads * i;
+      const int row = ci / ROWCH, col = ci % ROWCH;
+      const int hb = row >> 4, slot = row & 15;
+      const int id = hb ? id1 : id0;
+      const bool ok = (unsigned)id < (unsigned)a.num_blocks;
+      sreal[i] = ok && (blk0 + hb) * kTok + slot < n_ctx;
+      const size_t off = (ok ? (size_t)id * block_bytes : 0) + (size_t)(((slot * a.hkv + g) * D + col * 8) * 2);
+      sk[i] = *reinterpret_cast<const uint4 *>(kbase + off);
+      sv[i] = *reinterpret_cast<const uint4 *>(vbase + off);
+    }
+  };
+  auto stage_store = [&](int st) {
+    char *base = s_kv + st * WC::STAGE;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + kCThreads * i;
+      const int row = ci / ROWCH, col = ci % ROWCH;
+      const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
+                                                        // whole vector would go through memory
+      *reinterpret_cast<uint4 *>(base + row * RS + col * 16) =
+          make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk);
+      *reinterpret_cast<uint4 *>(base + (32 + row) * RS + col * 16) =
+          make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk);
+    }
+  };
+
+  // ---- one pair for the wave's four tiles, from LDS stage st
+  auto compute = [&](int pair, int st) {
+    const int blk0 = 2 * pair;
+    if (!has_rows || blk0 * kTok > plast) return;  // nothing of the pair is visible to the wave
+    bool ok[2];
+    ok[0] = (unsigned)block_id(blk0) < (unsigned)a.num_blocks;
+    ok[1] = (unsigned)block_id(blk0 + 1) < (unsigned)a.num_blocks;
+    const bool full = ok[0] && ok[1] && (blk0 + 2) * kTok - 1 <= pfirst;
+    const char *lk = s_kv + st * WC::STAGE;
+    const char *lv = lk + 32 * RS;
+    // A operands of S^T (token c of block hb, dims 32m + 8q .. +7) and the
+    // V rows 4q .. 4q+3 of each block at dims EV*c .. EV*c + EV - 1
+    uint4 kop[2][KM];
+    uint32_t vr[2][4][VDW];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+        kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + (16 * hb + c) * RS + (32 * m + 8 * q) * 2);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_dwords<VDW>(lv + (16 * hb + 4 * q + j) * RS + EV * c * 2, vr[hb][j]);
+    bf16x8_t va[EV];
+#pragma unroll
+    for (int m = 0; m < EV; ++m) {
+      uint32_t d4[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int hb = k2 >> 1, j0 = (k2 & 1) * 2;
+        d4[k2] = __builtin_amdgcn_perm(vr[hb][j0 + 1][m >> 1], vr[hb][j0][m >> 1],
+                                       (m & 1) ? 0x07060302u : 0x05040100u);
+      }
+      va[m] = as_bf16x8(make_uint4(d4[0], d4[1], d4[2], d4[3]));
+    }
+#pragma unroll
+    for (int t = 0; t < kWT; ++t) {
+      f32x4_t s[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        s[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+          s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[t][m], s[hb], 0, 0, 0);
+      }
+      float x[2][4];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[hb][j] = s[hb][j] * sl2;
+      float mx = max8(x);
+      if (!full) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int tok0 = (blk0 + hb) * kTok + 4 * q;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            x[hb][j] = (ok[hb] && tok0 + j <= prow[t]) ? x[hb][j] : -__builtin_huge_valf();
+        }
+        mx = max8(x);
+      }
+      mx = max4q(mx);
+      const bool raise = mx > mrun[t] + kLag;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mn = raise ? mx : mrun[t];
+        const float f = raise ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
+        mrun[t] = mn;
+        l4[t] *= f;
+#pragma unroll
+        for (int m = 0; m < EV; ++m) o[t][m] *= f;
+      }
+      const float nm = -mrun[t];
+      bf16x8_t pw;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[hb][j] + nm);
+      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pw, l4[t], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < EV; ++m)
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: every wave takes part in the staging and the barriers,
+  // also when none of a pair's tokens is visible to its rows
+  if (npairs > 0) {
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+    for (int p = 0; p < npairs; ++p) {
+      const int st = p & 1;
+      const bool more = p + 1 < npairs;
+      if (more) stage_load(p + 1);
+      compute(p, st);
+      // stage st ^ 1 was last read in the previous pass, before its barrier
+      if (more) stage_store(st ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- normalise and write the wave's rows: lane (c, q) holds dims
+  // 4*EV*q .. 4*EV*q + 4*EV - 1 of row c of each tile
+  if (!has_rows) return;
+#pragma unroll
+  for (int t = 0; t < kWT; ++t) {
+    const int r = wrow0 + 16 * t + c;
+    if (r < nrows) {
+      const float L = l4[t][0];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      float *op = a.out + ((size_t)(r0 + r / G) * a.hq + g * G + r % G) * D + 4 * EV * q;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int m = 0; m < EV; m += 4)
+          *reinterpret_cast<float4 *>(op + EV * rr + m) =
+              make_float4(o[t][m][rr] * inv, o[t][m + 1][rr] * inv, o[t][m + 2][rr] * inv, o[t][m + 3][rr] * inv);
+    }
+  }
+}
+
 
 template <int D, int G>
 hipError_t chunk_by_tiles(const ChunkArgs &a, unsigned grid, hipStream_t s) {
@@ -365,9 +649,8 @@ hipError_t chunk_by_tiles(const ChunkArgs &a, unsigned grid, hipStream_t s) {
     hipLaunchKernelGGL((chunk_kernel<D, G, 1>), dim3(grid), dim3(kCThreads), 0, s, a);
   } else if (a.nqt == 2) {
     hipLaunchKernelGGL((chunk_kernel<D, G, 2>), dim3(grid), dim3(kCThreads), 0, s, a);
-  } else if constexpr (max_tiles(D) >= 4) {
-    if (a.nqt != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_kernel<D, G, 4>), dim3(grid), dim3(kCThreads), 0, s, a);
+  } else if (a.nqt == kWideRows / 16) {
+    hipLaunchKernelGGL((chunk_wide_kernel<D, G>), dim3(grid), dim3(kCThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -389,7 +672,8 @@ hipError_t chunk_by_group(const ChunkArgs &a, unsigned grid, hipStream_t s) {
 
 int chunk_tiles_per_item(int max_q, int group, int d) {
   const long long rows = (long long)max_q * group;
-  return rows <= 16 ? 1 : (rows <= 256 ? 2 : max_tiles(d));
+  (void)d;
+  return rows <= 16 ? 1 : (rows <= 256 ? 2 : kWideRows / 16);
 }
 
 int chunk_items_per_head(int max_q, int group, int nqt) {

@@ -106,13 +106,32 @@ def test_chunk_small_shapes(d, hq, hkv):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("nq", [2, 4, 9, 64, 200])
 def test_chunk_tile_shapes(d, nq):
-    """Each rows-per-workgroup choice (16, 32, and 64 for head_dim 64), with
-    a partial last tile."""
+    """Each rows-per-workgroup choice (16, 32, and 256 rows staged through
+    LDS), with a partial last tile."""
     ctx = (300, 257, nq)
     base = make_inputs(_spec("chunk-tiles", d, 8, 2, ctx, 900 + d + nq), poison=True)
     ci = chunk_queries(base, [nq, nq, nq], 950 + nq)
     say(f"[chunk] tiles d={d} nq={nq}")
     assert_parity(ci, gpu_chunk(ci))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", GROUPS)
+def test_chunk_wide_shapes(d, hq, hkv):
+    """More than 256 rows per sequence (256-row workgroups, K/V staged in
+    LDS): partial last workgroups, a short sequence in the same launch, rows
+    before position zero, ragged block tails; unused slots and blocks hold
+    NaN."""
+    ctx = (700, 300, 129, 1000, 40)
+    nq = (300, 300, 129, 17, 60)
+    base = make_inputs(_spec("chunk-wide", d, hq, hkv, ctx, 1100 + d + hq + hkv), poison=True)
+    ci = chunk_queries(base, nq, 1150 + d + hq)
+    say(f"[chunk] wide d={d} hq={hq} hkv={hkv} rows={ci.total_rows}")
+    got = gpu_chunk(ci)
+    r4 = int(ci.q_start[4])
+    assert np.all(got[r4:r4 + 20] == 0.0)
+    err = assert_parity(ci, got)
+    say(f"  max err {err:.2e}")
 
 
 def test_chunk_rows_before_position_zero():
