@@ -20,10 +20,15 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled on purpose: the compiler would
 # otherwise pair independent fp32 operations into v_pk_* instructions.
+# MFMA accumulators are kept in arch VGPRs (-amdgpu-mfma-vgpr-form): in the
+# chunk kernels the compiler otherwise places them in AGPRs and copies all
+# of them to VGPRs and back on every loop iteration, for the rarely taken
+# rescaling of the online softmax.  Only the MFMA kernels are affected.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

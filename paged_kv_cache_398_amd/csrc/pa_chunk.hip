@@ -401,6 +401,9 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 constexpr int kWW = 4;                    // waves per workgroup
 constexpr int kWT = 4;                    // 16-row tiles per wave
 constexpr int kWideRows = kWW * kWT * 16; // rows per workgroup
+// tiles per softmax phase: as many as the registers allow without spilling
+template <int D>
+constexpr int phase_tiles() { return D == 64 ? 4 : 2; }
 
 template <int D>
 struct WideCfg {
@@ -417,6 +420,8 @@ __global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
   using WC = WideCfg<D>;
   constexpr int KM = C::KM, EV = C::EV, VDW = C::VDW;
   constexpr int RS = WC::RS, NCH = WC::NCH, ROWCH = WC::ROWCH;
+  constexpr int kPH = phase_tiles<D>();
+  static_assert(kWT % kPH == 0, "whole phases");
   static_assert(NCH >= 1 && NCH * kCThreads == 32 * ROWCH, "whole chunks per thread");
   static_assert(kWW * 64 == kCThreads, "one wave per 64 rows");
   __shared__ __align__(16) char s_kv[2 * WC::STAGE];
@@ -556,52 +561,77 @@ __global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
       }
       va[m] = as_bf16x8(make_uint4(d4[0], d4[1], d4[2], d4[3]));
     }
+    // the tiles in groups of kPH: all score products of a group first, then
+    // the softmax of all its tiles with one (rarely taken) rescaling branch,
+    // then all PV products -- a single basic block in the common case, so
+    // the scheduler can overlap one tile's VALU work with another's MFMAs
 #pragma unroll
-    for (int t = 0; t < kWT; ++t) {
-      f32x4_t s[2];
+    for (int t0 = 0; t0 < kWT; t0 += kPH) {
+      float x[kPH][2][4];
+      float mx[kPH];
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        s[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < KM; ++m)
-          s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[t][m], s[hb], 0, 0, 0);
-      }
-      float x[2][4];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[hb][j] = s[hb][j] * sl2;
-      float mx = max8(x);
-      if (!full) {
+      for (int u = 0; u < kPH; ++u) {
+        f32x4_t s[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const int tok0 = (blk0 + hb) * kTok + 4 * q;
+          s[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            x[hb][j] = (ok[hb] && tok0 + j <= prow[t]) ? x[hb][j] : -__builtin_huge_valf();
+          for (int m = 0; m < KM; ++m)
+            s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[t0 + u][m], s[hb], 0, 0, 0);
         }
-        mx = max8(x);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[u][hb][j] = s[hb][j] * sl2;
+        mx[u] = max8(x[u]);
       }
-      mx = max4q(mx);
-      const bool raise = mx > mrun[t] + kLag;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float mn = raise ? mx : mrun[t];
-        const float f = raise ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
-        mrun[t] = mn;
-        l4[t] *= f;
+      if (!full) {
 #pragma unroll
-        for (int m = 0; m < EV; ++m) o[t][m] *= f;
+        for (int u = 0; u < kPH; ++u) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int tok0 = (blk0 + hb) * kTok + 4 * q;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              x[u][hb][j] = (ok[hb] && tok0 + j <= prow[t0 + u]) ? x[u][hb][j] : -__builtin_huge_valf();
+          }
+          mx[u] = max8(x[u]);
+        }
       }
-      const float nm = -mrun[t];
-      bf16x8_t pw;
+      bool raise[kPH];
+      bool any = false;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int u = 0; u < kPH; ++u) {
+        mx[u] = max4q(mx[u]);
+        raise[u] = mx[u] > mrun[t0 + u] + kLag;
+        any = any || raise[u];
+      }
+      if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[hb][j] + nm);
-      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pw, l4[t], 0, 0, 0);
+        for (int u = 0; u < kPH; ++u) {
+          const int t = t0 + u;
+          const float mn = raise[u] ? mx[u] : mrun[t];
+          const float f = raise[u] ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
+          mrun[t] = mn;
+          l4[t] *= f;
 #pragma unroll
-      for (int m = 0; m < EV; ++m)
-        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
+          for (int m = 0; m < EV; ++m) o[t][m] *= f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPH; ++u) {
+        const int t = t0 + u;
+        const float nm = -mrun[t];
+        bf16x8_t pw;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[u][hb][j] + nm);
+        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pw, l4[t], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < EV; ++m)
+          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
+      }
     }
   };
 
