@@ -18,9 +18,9 @@
 //    verification): the four waves split the item's visible blocks in pairs
 //    (wave w takes pairs w, w + 4, ...), loading K/V straight into
 //    registers, and are combined exactly in LDS at the end;
-//  - chunk_wide_kernel, 256 rows per item (long prefill chunks): each wave
-//    owns 64 rows for the whole context, and every pair of blocks is staged
-//    once per workgroup in LDS, from where the four waves read it.
+//  - chunk_wide_kernel, 256 rows per item (long prefill chunks): eight
+//    waves each own 32 rows for the whole context, and every pair of blocks
+//    is staged once per workgroup in LDS, from where all of them read it.
 //
 // In both, the products run on the matrix cores (v_mfma_f32_16x16x32_bf16),
 // transposed so that every lane holds one query row throughout:
@@ -389,41 +389,44 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Long chunks.  One workgroup per kWideRows query rows of a (sequence, KV
-// head); each wave owns 64 of them (four 16-row tiles) over the whole
-// visible context, so no combine across waves is needed.  Every 32-token
-// pair of blocks is staged once per workgroup in LDS (two stages, one
-// barrier per pair; the next pair's global loads are in flight while the
-// current one is computed) and the four waves read their MFMA operands from
+// head); each of its eight waves owns 32 of them (two 16-row tiles) over the
+// whole visible context, so no combine across waves is needed.  Every
+// 32-token pair of blocks is staged once per workgroup in LDS (two stages,
+// one barrier per pair; the next pair's global loads are in flight while
+// the current one is computed) and the waves read their MFMA operands from
 // there: a K/V byte brought to the CU serves 256 rows, a byte read from LDS
-// serves the wave's 64.  The products, masks and online softmax per 16-row
-// tile are those of chunk_kernel.
+// serves the wave's 32.  Two waves per SIMD let one wave's softmax (VALU)
+// run beside the other's products (MFMA); with four waves of 64 rows, one
+// per SIMD, the two mostly took turns.  The products, masks and online
+// softmax per 16-row tile are those of chunk_kernel.
 
-constexpr int kWW = 4;                    // waves per workgroup
-constexpr int kWT = 4;                    // 16-row tiles per wave
+constexpr int kWW = 8;                    // waves per workgroup (two per SIMD)
+constexpr int kWT = 16 / kWW;             // 16-row tiles per wave
+constexpr int kWThreads = kWW * 64;
 constexpr int kWideRows = kWW * kWT * 16; // rows per workgroup
 // tiles per softmax phase: as many as the registers allow without spilling
 template <int D>
-constexpr int phase_tiles() { return D == 64 ? 4 : 2; }
+constexpr int phase_tiles() { return (D == 64 ? 4 : 2) < kWT ? (D == 64 ? 4 : 2) : kWT; }
 
 template <int D>
 struct WideCfg {
   static constexpr int RS = D * 2 + 16;                // LDS row stride (bytes); the 16 B of padding
                                                        // put the rows read together on distinct banks
   static constexpr int ROWCH = D / 8;                  // 16-byte chunks per token row
-  static constexpr int NCH = 32 * ROWCH / kCThreads;   // chunks per thread per pair (K, and V)
+  static constexpr int NCH = (32 * ROWCH + kWThreads - 1) / kWThreads;  // chunks per thread per pair (K, and V)
+  static constexpr bool ALL = 32 * ROWCH % kWThreads == 0;             // every thread has NCH chunks
   static constexpr int STAGE = 2 * 32 * RS;            // one pair: 32 K rows, then 32 V rows
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW / 4))) void chunk_wide_kernel(ChunkArgs a) {
   using C = ChunkCfg<D>;
   using WC = WideCfg<D>;
   constexpr int KM = C::KM, EV = C::EV, VDW = C::VDW;
   constexpr int RS = WC::RS, NCH = WC::NCH, ROWCH = WC::ROWCH;
   constexpr int kPH = phase_tiles<D>();
   static_assert(kWT % kPH == 0, "whole phases");
-  static_assert(NCH >= 1 && NCH * kCThreads == 32 * ROWCH, "whole chunks per thread");
-  static_assert(kWW * 64 == kCThreads, "one wave per 64 rows");
+  constexpr bool ALL = WC::ALL;
   __shared__ __align__(16) char s_kv[2 * WC::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -452,10 +455,10 @@ __global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
   const int npairs = (nblk + 1) / 2;
 
   // ---- the wave's rows
-  const int wrow0 = row0 + 64 * w;
+  const int wrow0 = row0 + 16 * kWT * w;
   const bool has_rows = wrow0 < nrows;
   const int pfirst = n_ctx - nq + wrow0 / G;                       // first row's position
-  const int plast = n_ctx - nq + (min(wrow0 + 64, nrows) - 1) / G;  // last row's position
+  const int plast = n_ctx - nq + (min(wrow0 + 16 * kWT, nrows) - 1) / G;  // last row's position
 
   bf16x8_t qf[kWT][KM];
   int prow[kWT];
@@ -495,12 +498,16 @@ __global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
   // into the products.
   uint4 sk[NCH], sv[NCH];
   bool sreal[NCH];
+  bool sall = true;  // every slot of the pair real (wave-uniform)
   auto stage_load = [&](int pair) {
     const int blk0 = 2 * pair;
     const int id0 = block_id(blk0), id1 = block_id(blk0 + 1);
+    sall = (unsigned)id0 < (unsigned)a.num_blocks && (unsigned)id1 < (unsigned)a.num_blocks &&
+           (blk0 + 2) * kTok <= n_ctx;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + kCThreads * i;
+      const int ci = tid + kWThreads * i;
+      if (!ALL && ci >= 32 * ROWCH) break;
       const int row = ci / ROWCH, col = ci % ROWCH;
       const int hb = row >> 4, slot = row & 15;
       const int id = hb ? id1 : id0;
@@ -513,9 +520,21 @@ __global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
   };
   auto stage_store = [&](int st) {
     char *base = s_kv + st * WC::STAGE;
+    if (sall) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = tid + kWThreads * i;
+        if (!ALL && ci >= 32 * ROWCH) break;
+        const int row = ci / ROWCH, col = ci % ROWCH;
+        *reinterpret_cast<uint4 *>(base + row * RS + col * 16) = sk[i];
+        *reinterpret_cast<uint4 *>(base + (32 + row) * RS + col * 16) = sv[i];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + kCThreads * i;
+      const int ci = tid + kWThreads * i;
+      if (!ALL && ci >= 32 * ROWCH) break;
       const int row = ci / ROWCH, col = ci % ROWCH;
       const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
                                                         // whole vector would go through memory
@@ -526,7 +545,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_wide_kernel(ChunkArgs a) {
     }
   };
 
-  // ---- one pair for the wave's four tiles, from LDS stage st
+  // ---- one pair for the wave's tiles, from LDS stage st
   auto compute = [&](int pair, int st) {
     const int blk0 = 2 * pair;
     if (!has_rows || blk0 * kTok > plast) return;  // nothing of the pair is visible to the wave
@@ -680,7 +699,7 @@ hipError_t chunk_by_tiles(const ChunkArgs &a, unsigned grid, hipStream_t s) {
   } else if (a.nqt == 2) {
     hipLaunchKernelGGL((chunk_kernel<D, G, 2>), dim3(grid), dim3(kCThreads), 0, s, a);
   } else if (a.nqt == kWideRows / 16) {
-    hipLaunchKernelGGL((chunk_wide_kernel<D, G>), dim3(grid), dim3(kCThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_wide_kernel<D, G>), dim3(grid), dim3(kWThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
