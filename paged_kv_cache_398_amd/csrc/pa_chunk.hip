@@ -391,9 +391,10 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 // Long chunks.  One workgroup per kWideRows query rows of a (sequence, KV
 // head); each of its eight waves owns 32 of them (two 16-row tiles) over the
 // whole visible context, so no combine across waves is needed.  Every
-// 32-token pair of blocks is staged once per workgroup in LDS (two stages,
-// one barrier per pair; the next pair's global loads are in flight while
-// the current one is computed) and the waves read their MFMA operands from
+// 64 tokens (four blocks) are staged once per workgroup in LDS (two stages,
+// one barrier per stage; the next stage's global loads are in flight while
+// the current one is computed, as two 32-token pairs) and the waves read
+// their MFMA operands from
 // there: a K/V byte brought to the CU serves 256 rows, a byte read from LDS
 // serves the wave's 32.  Two waves per SIMD let one wave's softmax (VALU)
 // run beside the other's products (MFMA); with four waves of 64 rows, one
@@ -404,18 +405,22 @@ constexpr int kWW = 8;                    // waves per workgroup (two per SIMD)
 constexpr int kWT = 16 / kWW;             // 16-row tiles per wave
 constexpr int kWThreads = kWW * 64;
 constexpr int kWideRows = kWW * kWT * 16; // rows per workgroup
+constexpr int kSB = 4;                    // blocks per LDS stage (two pairs)
+constexpr int kSR = kSB * 16;             // token rows per stage
 // tiles per softmax phase: as many as the registers allow without spilling
 template <int D>
 constexpr int phase_tiles() { return (D == 64 ? 4 : 2) < kWT ? (D == 64 ? 4 : 2) : kWT; }
 
 template <int D>
 struct WideCfg {
-  static constexpr int RS = D * 2 + 16;                // LDS row stride (bytes); the 16 B of padding
-                                                       // put the rows read together on distinct banks
+  // LDS row stride (bytes): 64 B of padding per row.  Rows read together
+  // then start on different banks; measured on the prefill chunk, 32 or 64 B
+  // of padding ran 5-10% faster than 16 B.
+  static constexpr int RS = D * 2 + 64;
   static constexpr int ROWCH = D / 8;                  // 16-byte chunks per token row
-  static constexpr int NCH = (32 * ROWCH + kWThreads - 1) / kWThreads;  // chunks per thread per pair (K, and V)
-  static constexpr bool ALL = 32 * ROWCH % kWThreads == 0;             // every thread has NCH chunks
-  static constexpr int STAGE = 2 * 32 * RS;            // one pair: 32 K rows, then 32 V rows
+  static constexpr int NCH = (kSR * ROWCH + kWThreads - 1) / kWThreads;  // chunks per thread per stage (K, and V)
+  static constexpr bool ALL = kSR * ROWCH % kWThreads == 0;             // every thread has NCH chunks
+  static constexpr int STAGE = 2 * kSR * RS;           // one stage: kSR K rows, then kSR V rows
 };
 
 template <int D, int G>
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   const int last_row = min(row0 + kWideRows, nrows) - 1;
   const int pmax = n_ctx - nq + last_row / G;
   const int nblk = pmax >= 0 ? pmax / kTok + 1 : 0;
-  const int npairs = (nblk + 1) / 2;
+  const int nstages = (nblk + kSB - 1) / kSB;
 
   // ---- the wave's rows
   const int wrow0 = row0 + 16 * kWT * w;
@@ -491,29 +496,35 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   const char *vbase = static_cast<const char *>(a.v_cache);
   auto block_id = [&](int blk) { return blk < nblk ? trow[blk] : -1; };
 
-  // ---- staging: thread tid moves chunks tid, tid + 256, ... of the pair's
-  // 32 K rows and 32 V rows (16 chunks of 16 B per row for head_dim 128).
+  // ---- staging: thread tid moves chunks tid, tid + 512, ... of the stage's
+  // kSR K rows and kSR V rows (16 chunks of 16 B per row for head_dim 128).
   // Slots past the cached tokens and blocks outside the pool are stored as
   // zeros: their scores are masked anyway, and V garbage (NaN) cannot leak
   // into the products.
   uint4 sk[NCH], sv[NCH];
   bool sreal[NCH];
-  bool sall = true;  // every slot of the pair real (wave-uniform)
-  auto stage_load = [&](int pair) {
-    const int blk0 = 2 * pair;
-    const int id0 = block_id(blk0), id1 = block_id(blk0 + 1);
-    sall = (unsigned)id0 < (unsigned)a.num_blocks && (unsigned)id1 < (unsigned)a.num_blocks &&
-           (blk0 + 2) * kTok <= n_ctx;
+  bool sall = true;  // every slot of the stage real (wave-uniform)
+  auto stage_load = [&](int sg) {
+    const int blk0 = kSB * sg;
+    int id[kSB];
+    sall = (blk0 + kSB) * kTok <= n_ctx;
+#pragma unroll
+    for (int h = 0; h < kSB; ++h) {
+      id[h] = block_id(blk0 + h);
+      sall = sall && (unsigned)id[h] < (unsigned)a.num_blocks;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ci = tid + kWThreads * i;
-      if (!ALL && ci >= 32 * ROWCH) break;
+      if (!ALL && ci >= kSR * ROWCH) break;
       const int row = ci / ROWCH, col = ci % ROWCH;
       const int hb = row >> 4, slot = row & 15;
-      const int id = hb ? id1 : id0;
-      const bool ok = (unsigned)id < (unsigned)a.num_blocks;
+      int bid = id[0];
+#pragma unroll
+      for (int h = 1; h < kSB; ++h) bid = hb == h ? id[h] : bid;
+      const bool ok = (unsigned)bid < (unsigned)a.num_blocks;
       sreal[i] = ok && (blk0 + hb) * kTok + slot < n_ctx;
-      const size_t off = (ok ? (size_t)id * block_bytes : 0) + (size_t)(((slot * a.hkv + g) * D + col * 8) * 2);
+      const size_t off = (ok ? (size_t)bid * block_bytes : 0) + (size_t)(((slot * a.hkv + g) * D + col * 8) * 2);
       sk[i] = *reinterpret_cast<const uint4 *>(kbase + off);
       sv[i] = *reinterpret_cast<const uint4 *>(vbase + off);
     }
@@ -524,37 +535,36 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int ci = tid + kWThreads * i;
-        if (!ALL && ci >= 32 * ROWCH) break;
+        if (!ALL && ci >= kSR * ROWCH) break;
         const int row = ci / ROWCH, col = ci % ROWCH;
         *reinterpret_cast<uint4 *>(base + row * RS + col * 16) = sk[i];
-        *reinterpret_cast<uint4 *>(base + (32 + row) * RS + col * 16) = sv[i];
+        *reinterpret_cast<uint4 *>(base + (kSR + row) * RS + col * 16) = sv[i];
       }
       return;
     }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ci = tid + kWThreads * i;
-      if (!ALL && ci >= 32 * ROWCH) break;
+      if (!ALL && ci >= kSR * ROWCH) break;
       const int row = ci / ROWCH, col = ci % ROWCH;
       const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
                                                         // whole vector would go through memory
       *reinterpret_cast<uint4 *>(base + row * RS + col * 16) =
           make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk);
-      *reinterpret_cast<uint4 *>(base + (32 + row) * RS + col * 16) =
+      *reinterpret_cast<uint4 *>(base + (kSR + row) * RS + col * 16) =
           make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk);
     }
   };
 
-  // ---- one pair for the wave's tiles, from LDS stage st
-  auto compute = [&](int pair, int st) {
-    const int blk0 = 2 * pair;
-    if (!has_rows || blk0 * kTok > plast) return;  // nothing of the pair is visible to the wave
+  // ---- one pair (blocks blk0, blk0 + 1) for the wave's tiles, from its
+  // rows r0s .. r0s + 31 of LDS stage st
+  auto compute = [&](int blk0, int st, int r0s) {
     bool ok[2];
     ok[0] = (unsigned)block_id(blk0) < (unsigned)a.num_blocks;
     ok[1] = (unsigned)block_id(blk0 + 1) < (unsigned)a.num_blocks;
     const bool full = ok[0] && ok[1] && (blk0 + 2) * kTok - 1 <= pfirst;
-    const char *lk = s_kv + st * WC::STAGE;
-    const char *lv = lk + 32 * RS;
+    const char *lk = s_kv + st * WC::STAGE + r0s * RS;
+    const char *lv = lk + kSR * RS;
     // A operands of S^T (token c of block hb, dims 32m + 8q .. +7) and the
     // V rows 4q .. 4q+3 of each block at dims EV*c .. EV*c + EV - 1
     uint4 kop[2][KM];
@@ -655,16 +665,22 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   };
 
   // ---- main loop: every wave takes part in the staging and the barriers,
-  // also when none of a pair's tokens is visible to its rows
-  if (npairs > 0) {
+  // also when none of a stage's tokens is visible to its rows
+  if (nstages > 0) {
     stage_load(0);
     stage_store(0);
     __syncthreads();
-    for (int p = 0; p < npairs; ++p) {
-      const int st = p & 1;
-      const bool more = p + 1 < npairs;
-      if (more) stage_load(p + 1);
-      compute(p, st);
+    for (int sg = 0; sg < nstages; ++sg) {
+      const int st = sg & 1;
+      const bool more = sg + 1 < nstages;
+      if (more) stage_load(sg + 1);
+#pragma unroll
+      for (int sp = 0; sp < kSB / 2; ++sp) {
+        const int blk0 = kSB * sg + 2 * sp;
+        // nothing of the pair (or of the ones after it) visible to the wave
+        if (!has_rows || blk0 * kTok > plast) break;
+        compute(blk0, st, 32 * sp);
+      }
       // stage st ^ 1 was last read in the previous pass, before its barrier
       if (more) stage_store(st ^ 1);
       __syncthreads();
