@@ -266,8 +266,10 @@ def test_chunk_errors():
 @pytest.mark.parametrize("d,hq,max_q,rows,per_head", [
     (128, 8, 4, 16, 1),      # 4 tokens x G 4 = 16 rows: one tile
     (128, 8, 5, 32, 1),      # 20 rows: two tiles
-    (128, 8, 2048, 32, 256),  # head_dim 128: at most two tiles per workgroup
-    (64, 8, 2048, 64, 128),  # head_dim 64: four
+    (128, 8, 64, 32, 8),     # 256 rows: still 32-row workgroups
+    (128, 8, 65, 256, 2),    # 260 rows: 256-row workgroups (K/V staged in LDS)
+    (128, 8, 2048, 256, 32),  # a 2048-token prefill chunk
+    (64, 8, 2048, 256, 32),  # the same for head_dim 64
     (64, 16, 1, 16, 1),      # G 8, one token
     (128, 2, 100, 32, 4),    # G 1: 100 rows, two tiles -> 4 workgroups per head
     (128, 8, 0, 16, 0),
