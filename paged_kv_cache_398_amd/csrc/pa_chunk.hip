@@ -41,7 +41,10 @@
 //    16 lanes) and the EV products take element m of each: product m covers
 //    dims EV*rho + m, rho = 0..15.  The accumulator then gives lane (c, q)
 //    dims 4*EV*q .. 4*EV*q + 4*EV - 1 of row c.  The V^T operands are
-//    built by byte permutes once per pair, shared by the row tiles.
+//    built by byte permutes once per pair, shared by the row tiles.  (The
+//    wide kernel instead computes O = P V with A = the same P registers and
+//    B = V read from LDS by transposing reads, no permutes; a lane then
+//    holds one dimension of four rows.)
 //  - The row sums l come out of the matrix cores too: one more product per
 //    tile with A = all ones gives every lane the sum of its row's weights.
 //
@@ -68,6 +71,8 @@ constexpr float kNoMax = -3.402823466e38f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
 template <int D>
 struct ChunkCfg {
@@ -409,7 +414,7 @@ constexpr int kSB = 4;                    // blocks per LDS stage (two pairs)
 constexpr int kSR = kSB * 16;             // token rows per stage
 // tiles per softmax phase: as many as the registers allow without spilling
 template <int D>
-constexpr int phase_tiles() { return (D == 64 ? 4 : 2) < kWT ? (D == 64 ? 4 : 2) : kWT; }
+constexpr int phase_tiles() { return D == 64 ? kWT : 1; }
 
 template <int D>
 struct WideCfg {
@@ -433,6 +438,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   static_assert(kWT % kPH == 0, "whole phases");
   constexpr bool ALL = WC::ALL;
   __shared__ __align__(16) char s_kv[2 * WC::STAGE];
+  __shared__ __align__(16) float s_f[kWW][16];  // per-row rescaling factors
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -565,30 +571,28 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     const bool full = ok[0] && ok[1] && (blk0 + 2) * kTok - 1 <= pfirst;
     const char *lk = s_kv + st * WC::STAGE + r0s * RS;
     const char *lv = lk + kSR * RS;
-    // A operands of S^T (token c of block hb, dims 32m + 8q .. +7) and the
-    // V rows 4q .. 4q+3 of each block at dims EV*c .. EV*c + EV - 1
+    // A operands of S^T: token c of block hb, dims 32m + 8q .. +7
     uint4 kop[2][KM];
-    uint32_t vr[2][4][VDW];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int m = 0; m < KM; ++m)
         kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + (16 * hb + c) * RS + (32 * m + 8 * q) * 2);
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) load_dwords<VDW>(lv + (16 * hb + 4 * q + j) * RS + EV * c * 2, vr[hb][j]);
-    bf16x8_t va[EV];
+    // B operands of O = P V, one per 16 dims (slab m): lane (n = c, q)
+    // needs V[token 4q + e of block hb][dim 16m + n] for e = 0..3, hb = 0, 1.
+    // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of
+    // the 8 bytes addressed by lanes 4r + i / 4, r = 0..3 (checked on the
+    // GPU with a one-wave probe); so lane 4r + s addresses token 4q + r,
+    // dims 16m + 4s .. 16m + 4s + 3, of the row-major V rows in LDS.
+    bf16x8_t vb[EV];
 #pragma unroll
     for (int m = 0; m < EV; ++m) {
-      uint32_t d4[4];
+      v4s_t h[2];
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const int hb = k2 >> 1, j0 = (k2 & 1) * 2;
-        d4[k2] = __builtin_amdgcn_perm(vr[hb][j0 + 1][m >> 1], vr[hb][j0][m >> 1],
-                                       (m & 1) ? 0x07060302u : 0x05040100u);
-      }
-      va[m] = as_bf16x8(make_uint4(d4[0], d4[1], d4[2], d4[3]));
+      for (int hb = 0; hb < 2; ++hb)
+        h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RS + (16 * m + 4 * (c & 3)) * 2));
+      vb[m] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // the tiles in groups of kPH: all score products of a group first, then
     // the softmax of all its tiles with one (rarely taken) rescaling branch,
@@ -642,9 +646,22 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
           const float mn = raise[u] ? mx[u] : mrun[t];
           const float f = raise[u] ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
           mrun[t] = mn;
-          l4[t] *= f;
+          // lane (c, q) holds the factor of row c; its O and l entries are
+          // rows 4q .. 4q+3: fetch those rows' factors from lanes 4q + r
+          // through LDS: row c's lanes write it, then every lane reads its
+          // four rows' factors at once (cross-lane permutes per row kept
+          // more registers live and made the kernel spill)
+          if (q == 0) s_f[w][c] = f;
+          __builtin_amdgcn_wave_barrier();
+          const float4 f4 = *reinterpret_cast<const float4 *>(&s_f[w][4 * q]);
+          __builtin_amdgcn_wave_barrier();
+          const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-          for (int m = 0; m < EV; ++m) o[t][m] *= f;
+          for (int r = 0; r < 4; ++r) {
+            l4[t][r] *= fr[r];
+#pragma unroll
+            for (int m = 0; m < EV; ++m) o[t][m][r] *= fr[r];
+          }
         }
       }
 #pragma unroll
@@ -656,10 +673,12 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[u][hb][j] + nm);
-        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pw, l4[t], 0, 0, 0);
+        // O = P V with A = P: lane (c, q)'s eight weights are row c's
+        // tokens 4q .. 4q+3 of both blocks, the same k order as vb
+        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pw, ones, l4[t], 0, 0, 0);
 #pragma unroll
         for (int m = 0; m < EV; ++m)
-          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
+          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pw, vb[m], o[t][m], 0, 0, 0);
       }
     }
   };
@@ -687,24 +706,22 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     }
   }
 
-  // ---- normalise and write the wave's rows: lane (c, q) holds dims
-  // 4*EV*q .. 4*EV*q + 4*EV - 1 of row c of each tile
+  // ---- normalise and write the wave's rows: lane (n = c, q) holds dim
+  // 16m + n of rows 4q .. 4q+3 of each tile (and those rows' sums)
   if (!has_rows) return;
 #pragma unroll
-  for (int t = 0; t < kWT; ++t) {
-    const int r = wrow0 + 16 * t + c;
-    if (r < nrows) {
-      const float L = l4[t][0];
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      float *op = a.out + ((size_t)(r0 + r / G) * a.hq + g * G + r % G) * D + 4 * EV * q;
+  for (int t = 0; t < kWT; ++t)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = wrow0 + 16 * t + 4 * q + rr;
+      if (r < nrows) {
+        const float L = l4[t][rr];
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float *op = a.out + ((size_t)(r0 + r / G) * a.hq + g * G + r % G) * D + c;
 #pragma unroll
-        for (int m = 0; m < EV; m += 4)
-          *reinterpret_cast<float4 *>(op + EV * rr + m) =
-              make_float4(o[t][m][rr] * inv, o[t][m + 1][rr] * inv, o[t][m + 2][rr] * inv, o[t][m + 3][rr] * inv);
+        for (int m = 0; m < EV; ++m) op[16 * m] = o[t][m][rr] * inv;
+      }
     }
-  }
 }
 
 
