@@ -10,6 +10,7 @@ combination of V values whose weights are off by at most a relative 2^-8:
 is evaluated with the oracle itself, by running it on |V|.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -132,6 +133,24 @@ def test_chunk_wide_shapes(d, hq, hkv):
     assert np.all(got[r4:r4 + 20] == 0.0)
     err = assert_parity(ci, got)
     say(f"  max err {err:.2e}")
+
+
+@pytest.mark.parametrize("scale", [1.0, -0.3, 0.0])
+def test_chunk_scale_extremes(scale):
+    """Softmax scales other than 1/sqrt(d) through each kernel (16, 32 and
+    256 rows per workgroup): 1.0 keeps raising the running maximum after the
+    first pair, so the accumulated rows are rescaled (in the wide kernel with
+    per-row factors gathered through LDS); a negative scale; 0 (uniform
+    weights, masked slots still contribute nothing)."""
+    ctx = (1000, 700, 300, 64)
+    base = dataclasses.replace(make_inputs(_spec("chunk-scale", 128, 8, 2, ctx, 1300), poison=True),
+                               scale=np.float32(scale))
+    dev = to_device(base)
+    for nq in ((4, 4, 4, 4), (40, 17, 40, 5), (300, 260, 129, 64)):
+        ci = chunk_queries(base, nq, 1310 + nq[0])
+        say(f"[chunk] scale={scale} rows/seq={nq}")
+        err = assert_parity(ci, gpu_chunk(ci, dev=dev))
+        say(f"  max err {err:.2e}")
 
 
 def test_chunk_rows_before_position_zero():

@@ -109,6 +109,34 @@ def test_kivi_decode_matches_oracle(bits, d, hq, hkv):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("scale", [1.0, -0.3, 0.0])
+def test_kivi_decode_scale_extremes(bits, scale):
+    """Softmax scales other than 1/sqrt(d): a sharp softmax whose running
+    maximum keeps rising (partial sums rescaled after the first block), a
+    negative scale, and 0 (uniform weights; slots past the tokens still
+    contribute nothing)."""
+    rng = np.random.Generator(np.random.PCG64(1400 + bits))
+    lens = [1000, 17, 700, 64, 16]
+    hq, hkv, d = 8, 2, 128
+    N = sum(n // BLOCK for n in lens) + 3
+    kc, vc, kp, vp, rk, rv = kivi_state(rng, N, len(lens), hkv, d, bits)
+    width = max(n // BLOCK for n in lens) + 2
+    table = _table(rng, lens, N, width)
+    q = _bf16_bits(rng.standard_normal((len(lens), hq, d)))
+    say(f"[kivi] scale={scale} bits={bits}")
+    g = Gpu(kc, vc, kp, vp, rk, rv, bits)
+    try:
+        g.tables(table, lens, max(lens))
+        got = g.decode(q, hq, float(np.float32(scale)))
+    finally:
+        g.close()
+    want = kivi.kivi_decode_attention(q, kc, vc, kp, vp, rk, rv, table, np.array(lens),
+                                      np.float32(scale), bits)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - want).max() <= 2e-3
+
+
+@pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("d", [64, 128])
 def test_kivi_append_matches_oracle_bytes(bits, d):
     rng = np.random.Generator(np.random.PCG64(2000 + bits + d))

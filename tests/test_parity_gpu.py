@@ -5,6 +5,7 @@ f32/bf16 KV with fp32 accumulation, 3e-2 for FP8 KV against an oracle that
 dequantises the same codes with the same scales.
 """
 
+import dataclasses
 import functools
 import math
 import sys
@@ -99,6 +100,27 @@ def test_context_edges(kv):
     for nwg in (0, 5, 17, 96):
         say(f"[parity] edges kv={kv} wg={nwg}")
         got = gpu_decode(inp, workgroups=nwg)
+        assert max_err(got, want) <= TOL[kv], nwg
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("scale", [1.0, -0.3, 0.0])
+def test_scale_extremes(kv, scale):
+    """Softmax scales other than 1/sqrt(d): 1.0 makes the softmax sharp and
+    its running maximum keep rising along the sequence, so partial sums are
+    rescaled after the first block (not only from zero); a negative scale
+    flips which score is largest; 0 gives uniform weights (masked slots must
+    still give exactly nothing).  Unsplit and split launch shapes."""
+    ctx = (1000, 17, 700, 64)
+    spec = Spec(name="scales", batch=len(ctx), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                kv_dtype=kv, q_dtype="f32" if kv == "f32" else "bf16", seed=1200,
+                context_lens=ctx)
+    inp = dataclasses.replace(make_inputs(spec, poison=True), scale=np.float32(scale))
+    want = oracle_decode(inp)
+    for nwg in (0, 7, 64):
+        say(f"[parity] scale={scale} kv={kv} wg={nwg}")
+        got = gpu_decode(inp, workgroups=nwg)
+        assert np.isfinite(got).all()
         assert max_err(got, want) <= TOL[kv], nwg
 
 
