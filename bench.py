@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV-read TB/s, % of 8 TB/s HBM peak; µs per decode step"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_398_amd", "csrc", "pa_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_398_amd", "csrc", f)
+               for f in ("pa_kernels.hip", "pa_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_kernel_llama3_8b_b32_ctx4k.json")
 
 
@@ -41,8 +42,12 @@ def log(msg):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the attention kernel's sources (kernel file and the header it includes)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def kv_bytes(inp):

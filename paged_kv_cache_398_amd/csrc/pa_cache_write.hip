@@ -112,7 +112,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
     char *base = static_cast<char *>(which == 0 ? a.k_cache : a.v_cache);
     const uint4 *from = reinterpret_cast<const uint4 *>(base + (size_t)src * a.block_bytes);
     uint4 *to = reinterpret_cast<uint4 *>(base + (size_t)dst * a.block_bytes);
-    for (int64_t k = threadIdx.x; k < n16; k += 256) to[k] = from[k];
+    for (int64_t k = threadIdx.x; k < n16; k += 256) {
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(from + k));
+      __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t *>(to + k));
+    }
     const int words = which == 0 ? a.k_par_words : a.v_par_words;
     if (words > 0) {
       uint32_t *par = static_cast<uint32_t *>(which == 0 ? a.k_par : a.v_par);

@@ -117,11 +117,11 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_ca
 template <int N>
 __device__ __forceinline__ void load_dwords(const char *p, uint32_t *dst) {
   if constexpr (N == 4) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    const uint4 x = load_stream16(p);
     dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
   } else {
     static_assert(N == 2, "8- or 16-byte slices");
-    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    const uint2 x = load_stream8(p);
     dst[0] = x.x; dst[1] = x.y;
   }
 }
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
       const char *kb = kbase + boff, *vb = vbase + boff;
 #pragma unroll
       for (int m = 0; m < KM; ++m)
-        P.k[hb][m] = *reinterpret_cast<const uint4 *>(kb + (k_off + 64 * m));
+        P.k[hb][m] = load_stream16(kb + (k_off + 64 * m));
 #pragma unroll
       for (int j = 0; j < 4; ++j) load_dwords<VDW>(vb + (v_off + j * v_step), P.v[hb][j]);
     }
@@ -432,7 +432,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW / 4))) void chunk_wide_kernel(ChunkArgs a) {
   using C = ChunkCfg<D>;
   using WC = WideCfg<D>;
-  constexpr int KM = C::KM, EV = C::EV, VDW = C::VDW;
+  constexpr int KM = C::KM, EV = C::EV;
   constexpr int RS = WC::RS, NCH = WC::NCH, ROWCH = WC::ROWCH;
   constexpr int kPH = phase_tiles<D>();
   static_assert(kWT % kPH == 0, "whole phases");

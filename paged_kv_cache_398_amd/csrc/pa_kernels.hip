@@ -129,14 +129,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-template <int CH>
+// NT: with the non-temporal hint.  FP8 pools are read without it: their
+// 128-byte rows (and 64-byte scale runs) sustained about 7% less bandwidth
+// with the hint than without, the opposite of the 2-byte pools.
+template <int CH, bool NT>
 __device__ __forceinline__ void load_chunk(const char *p, uint32_t *dst) {
   if constexpr (CH == 16) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    const uint4 x = NT ? load_stream16(p) : *reinterpret_cast<const uint4 *>(p);
     dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
   } else {
     static_assert(CH == 8, "8- or 16-byte loads only");
-    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    const uint2 x = NT ? load_stream8(p) : *reinterpret_cast<const uint2 *>(p);
     dst[0] = x.x; dst[1] = x.y;
   }
 }
@@ -284,8 +287,8 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
     for (int p = 0; p < NPASS; ++p) {
 #pragma unroll
       for (int c = 0; c < C::NCH; ++c) {
-        load_chunk<C::CH>(kb + (lane_off[p] + c * LPT * C::CH), &bk.k[p][c * (C::CH / 4)]);
-        load_chunk<C::CH>(vb + (lane_off[p] + c * LPT * C::CH), &bk.v[p][c * (C::CH / 4)]);
+        load_chunk<C::CH, KV != KV_FP8>(kb + (lane_off[p] + c * LPT * C::CH), &bk.k[p][c * (C::CH / 4)]);
+        load_chunk<C::CH, KV != KV_FP8>(vb + (lane_off[p] + c * LPT * C::CH), &bk.v[p][c * (C::CH / 4)]);
       }
       if constexpr (KV == KV_FP8) {
         const size_t si = ((bk.ok ? (size_t)phys : 0) * a.hkv + g) * kBlock + p * C::TPP + slot;

@@ -111,14 +111,14 @@ template <int N>
 __device__ __forceinline__ void load_dw(const char *p, uint32_t *dst) {
   static_assert(N == 1 || N % 2 == 0, "dword count");
   if constexpr (N == 1) {
-    dst[0] = *reinterpret_cast<const uint32_t *>(p);
+    dst[0] = load_stream4(p);
   } else if constexpr (N == 2) {
-    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    const uint2 x = load_stream8(p);
     dst[0] = x.x; dst[1] = x.y;
   } else {
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
-      const uint4 x = *reinterpret_cast<const uint4 *>(p + 4 * i);
+      const uint4 x = load_stream16(p + 4 * i);
       dst[i] = x.x; dst[i + 1] = x.y; dst[i + 2] = x.z; dst[i + 3] = x.w;
     }
   }
