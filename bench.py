@@ -140,7 +140,11 @@ def chunk_leg(name, iters, main_inp, main_pools):
     else:
         ci = make_chunk_inputs(name)
         dev = to_device(ci.base)
-        p = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+        bs = ci.base.spec
+        k, v = pa.allocate_kv_pools(ci.base.num_blocks, bs.num_kv_heads, bs.head_dim, "bf16")
+        k.copy_(dev.k_pool)
+        v.copy_(dev.v_pool)
+        p = pa.PagedKVPool(k, v, "bf16")
         p.set_block_table(dev.block_table, dev.context_lens, ci.base.max_context_len)
         own = pools = [p]
     s = ci.base.spec
@@ -370,8 +374,11 @@ def main():
     R = max(1, args.layers)
     pools = []
     for r in range(R):
-        k = dev.k_pool if r == 0 else dev.k_pool.clone()
-        v = dev.v_pool if r == 0 else dev.v_pool.clone()
+        # each layer's K and V pools in one buffer, placed as the library
+        # recommends (pa_kv_pool_placement: V shifted 256 B against K)
+        k, v = pa.allocate_kv_pools(inp.num_blocks, s.num_kv_heads, s.head_dim, s.kv_dtype)
+        k.copy_(dev.k_pool.view(k.dtype))
+        v.copy_(dev.v_pool.view(v.dtype))
         ks = None if dev.k_scale is None else (dev.k_scale if r == 0 else dev.k_scale.clone())
         vs = None if dev.v_scale is None else (dev.v_scale if r == 0 else dev.v_scale.clone())
         p = pa.PagedKVPool(k, v, s.kv_dtype, ks, vs)
@@ -502,6 +509,8 @@ def main():
             "kv_dtype": s.kv_dtype, "q_dtype": s.q_dtype, "out_dtype": "f32",
             "kv_bytes_per_step": nbytes, "workgroups": nwg,
             "layers_cycled": R, "kv_heads_per_workgroup": hc,
+            "kv_placement": "K and V pools of a layer in one buffer, V at a 2 KiB "
+                            "boundary + 256 B (pa_kv_pool_placement)",
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -38,11 +38,29 @@ from .binding import (  # noqa: F401
     pa_kv_pool_create,
     pa_kv_pool_create_kivi,
     pa_kv_pool_destroy,
+    pa_kv_pool_placement,
     pa_last_error,
     pa_profile_enable,
     pa_profile_read,
     pa_status_str,
 )
+
+
+def allocate_kv_pools(num_blocks, num_kv_heads, head_dim, kv_dtype, device="cuda"):
+    """K and V pools ``[num_blocks][16][num_kv_heads][head_dim]`` placed in
+    one device buffer as :func:`pa_kv_pool_placement` recommends (V shifted
+    by 256 B against K's 2 KiB address classes).  Returns ``(k, v)`` views
+    (float32, bfloat16, or uint8 for FP8 codes) that keep the buffer alive;
+    the contents are uninitialised."""
+    import torch  # device memory only
+
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[kv_dtype]
+    pool_bytes, v_off, total = pa_kv_pool_placement(num_blocks, num_kv_heads, head_dim, kv_dtype)
+    buf = torch.empty(total, dtype=torch.uint8, device=device)
+    shape = (num_blocks, PA_BLOCK_SIZE, num_kv_heads, head_dim)
+    k = buf[:pool_bytes].view(tdt).view(shape)
+    v = buf[v_off:v_off + pool_bytes].view(tdt).view(shape)
+    return k, v
 
 
 class PagedKVPool:

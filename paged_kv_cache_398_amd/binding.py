@@ -29,6 +29,8 @@ SIGNATURES = [
     ("pa_kv_pool_create", _i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                  ctypes.POINTER(_vp)]),
     ("pa_kv_pool_destroy", None, [_vp]),
+    ("pa_kv_pool_placement", _i32, [_i32, _i32, _i32, _i32, ctypes.POINTER(_sz),
+                                    ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     ("pa_block_table_set", _i32, [_vp, _vp, _vp, _i32, _i32, _i32]),
     ("pa_block_table_validate", _i32, [_vp, _vp]),
     ("pa_cache_append", _i32, [_vp, _vp, _vp, _i32, _vp]),
@@ -130,6 +132,16 @@ def pa_kv_pool_create(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype, 
                                             _dtype(kv_dtype), _ptr(k_cache), _ptr(v_cache),
                                             _ptr(k_scale), _ptr(v_scale), ctypes.byref(out)))
     return out.value
+
+
+def pa_kv_pool_placement(num_blocks, num_kv_heads, head_dim, kv_dtype) -> tuple:
+    """(pool_bytes, v_offset, total_bytes) of the recommended one-buffer
+    layout of a K and a V pool (include/pa.h)."""
+    pb, vo, tb = _sz(), _sz(), _sz()
+    _check(load_library().pa_kv_pool_placement(num_blocks, num_kv_heads, head_dim,
+                                               _dtype(kv_dtype), ctypes.byref(pb),
+                                               ctypes.byref(vo), ctypes.byref(tb)))
+    return pb.value, vo.value, tb.value
 
 
 def pa_kv_pool_destroy(pool: int) -> None:

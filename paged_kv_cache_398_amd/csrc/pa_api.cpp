@@ -319,6 +319,33 @@ pa_status pa_kv_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_
   return ok();
 }
 
+pa_status pa_kv_pool_placement(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype kv_dtype, size_t *pool_bytes, size_t *v_offset,
+                               size_t *total_bytes) {
+  if (!pool_bytes || !v_offset || !total_bytes)
+    return fail(PA_ERR_NULL, "pool_bytes, v_offset or total_bytes is NULL");
+  int64_t eb = 0;
+  switch (kv_dtype) {
+    case PA_DTYPE_F32: eb = 4; break;
+    case PA_DTYPE_BF16: eb = 2; break;
+    case PA_DTYPE_FP8_E4M3: eb = 1; break;
+    default: return fail(PA_ERR_DTYPE, "placement is for f32, bf16 and FP8 pools");
+  }
+  if (num_blocks < 1 || num_kv_heads < 1 || head_dim < 1)
+    return fail(PA_ERR_SHAPE, "num_blocks, num_kv_heads and head_dim must be positive");
+  const int64_t row = (int64_t)num_kv_heads * head_dim * eb * PA_BLOCK_SIZE;
+  if (row > ((int64_t)1 << 30) || (int64_t)num_blocks > (((int64_t)1 << 46) / row))
+    return fail(PA_ERR_SHAPE, "pool too large");
+  // 2 KiB period of the address classes, shifted by 256 B (see pa.h)
+  constexpr int64_t kPeriod = 2048, kShift = 256;
+  const int64_t bytes = row * num_blocks;
+  const int64_t voff = (bytes + kPeriod - 1) / kPeriod * kPeriod + kShift;
+  *pool_bytes = (size_t)bytes;
+  *v_offset = (size_t)voff;
+  *total_bytes = (size_t)(voff + bytes);
+  return ok();
+}
+
 void pa_kv_pool_destroy(pa_kv_pool *pool) {
   if (!pool) return;
   release_events(pool);

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 30
+    assert len(names) == 31
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -40,6 +40,24 @@ def _status(fn, *args, **kw):
     with pytest.raises(PAError) as ei:
         fn(*args, **kw)
     return ei.value.status
+
+
+def test_pool_placement():
+    # Llama-3-8B-shaped layer: 8192 blocks of 16 x 8 x 128 bf16 = 256 MiB per pool
+    pb, vo, tb = pa.pa_kv_pool_placement(8192, 8, 128, "bf16")
+    assert pb == 8192 * 16 * 8 * 128 * 2
+    assert vo == pb + 256 and tb == vo + pb
+    # a pool size that is not a multiple of 2 KiB is rounded up first
+    pb, vo, tb = pa.pa_kv_pool_placement(3, 1, 64, "fp8_e4m3")
+    assert pb == 3 * 16 * 64 and vo == 4096 + 256 and tb == vo + pb
+    for args in [(32, 2, 64, "f32"), (16384, 32, 128, "fp8_e4m3"), (7, 3, 128, "bf16")]:
+        pb, vo, tb = pa.pa_kv_pool_placement(*args)
+        assert vo % 2048 == 256 and vo >= pb and tb == vo + pb
+    c = pa.pa_kv_pool_placement
+    assert _status(c, 0, 8, 128, "bf16") == pa.binding.PA_ERR_SHAPE
+    assert _status(c, 8, 8, 128, "int8_kivi") == pa.binding.PA_ERR_DTYPE
+    lib = pa.load_library()
+    assert lib.pa_kv_pool_placement(8, 8, 128, 1, None, None, None) == pa.binding.PA_ERR_NULL
 
 
 def test_pool_create_errors():

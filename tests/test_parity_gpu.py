@@ -62,6 +62,32 @@ def test_named_workload(name):
     assert err <= TOL[inp.spec.kv_dtype]
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "llama3_8b_b32_ctx4k", "fp8_mha_b32_ctx8k"])
+def test_placed_pools(name):
+    """K and V pools in one buffer as pa_kv_pool_placement recommends (V at
+    a 2 KiB boundary + 256 B): bit-identical to separate pools, and within
+    the tolerance of the oracle."""
+    say(f"[parity] placed pools {name}: generating")
+    inp = named(name)
+    s = inp.spec
+    dev = to_device(inp)
+    k, v = pa.allocate_kv_pools(inp.num_blocks, s.num_kv_heads, s.head_dim, s.kv_dtype)
+    pool_bytes, v_off, _ = pa.pa_kv_pool_placement(inp.num_blocks, s.num_kv_heads,
+                                                   s.head_dim, s.kv_dtype)
+    assert v.data_ptr() - k.data_ptr() == v_off and v_off % 2048 == 256
+    k.copy_(dev.k_pool.view(k.dtype))
+    v.copy_(dev.v_pool.view(v.dtype))
+    placed = dataclasses.replace(dev, k_pool=k, v_pool=v)
+    say(f"[parity] placed pools {name}: gpu runs")
+    got = gpu_decode(inp, dev=placed)
+    ref = gpu_decode(inp, dev=dev)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    seqs = None if inp.logical_tokens <= 32 * 4096 else _sample_seqs(inp)
+    err = max_err(got, oracle_decode(inp, seqs), seqs)
+    say(f"[parity] placed pools {name}: max abs err {err:.3e}")
+    assert err <= TOL[s.kv_dtype]
+
+
 # ---------------------------------------------------------------------------
 # small shapes: several blocks and partitions, ragged tails, every build
 
