@@ -522,6 +522,8 @@ def main():
         "pct_of_hbm_peak": round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2),
         "cold": None if not cold else {
             "median_step_us": round(statistics.median(cold) * 1e6, 2),
+            "p10_step_us": round(float(np.percentile(cold, 10)) * 1e6, 2),
+            "p90_step_us": round(float(np.percentile(cold, 90)) * 1e6, 2),
             "tb_s": round(nbytes / statistics.median(cold) / 1e12, 4),
             "iters": len(cold),
             "note": "one step after reading 1 GiB elsewhere; event-timed step",
