@@ -353,9 +353,10 @@ pa_status pa_chunk_tiles(const pa_kv_pool *pool, int32_t num_q_heads, int32_t ma
  * between two or more workgroups.  Each piece of a split sequence leaves a
  * running max, a running sum and an unnormalised output per query head,
  * combined exactly (log-sum-exp) by the workgroup that finishes last.  The
- * workspace holds two such records per workgroup; its size depends on the
- * workgroup count and head chunk in force (pa_decode_workgroups,
- * pa_decode_heads_per_workgroup) and on num_q_heads, not on the lengths.
+ * workspace holds two such records per workgroup, sized for the widest head
+ * chunk a run may use; its size depends on the workgroup count, the head
+ * chunks (pa_decode_workgroups, pa_decode_heads_per_workgroup) and
+ * num_q_heads, not on the lengths.
  * *bytes receives the size (0 with a single workgroup).
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_SHAPE.
  */
@@ -424,16 +425,22 @@ pa_status pa_decode_workgroups(const pa_kv_pool *pool, int32_t *count);
  * divides num_kv_heads and is at most the workgroup's wave count (4).  Any
  * value gives the same result; it changes how many contiguous bytes of
  * each block one workgroup reads and how many workgroups there are.
- * Automatic choice: the largest chunk for which batch * num_kv_heads /
- * heads is still at least 256 (with equal context lengths, each
- * workgroup's share is then whole sequences), else the largest allowed.
+ * Automatic choice, made on the device from the lengths: when every
+ * sequence has the block count of max_context_len, the largest chunk for
+ * which batch * num_kv_heads / heads is still at least 256 (each
+ * workgroup's share is then whole sequences), else the largest allowed;
+ * when the block counts differ, the largest allowed (shares cut across
+ * sequences anyway, and fewer, longer pieces stream faster).  An override
+ * fixes the chunk for both cases.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE.
  */
 pa_status pa_decode_set_heads_per_workgroup(pa_kv_pool *pool, int32_t heads);
 
 /*
  * pa_decode_heads_per_workgroup -- head chunk the next run will use for the
- * table set last.
+ * table set last if every sequence has the block count of max_context_len
+ * (with differing block counts the run takes the largest allowed chunk,
+ * unless an override is set).
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set).
  */
 pa_status pa_decode_heads_per_workgroup(const pa_kv_pool *pool, int32_t *heads);

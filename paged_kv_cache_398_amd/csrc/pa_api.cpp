@@ -124,19 +124,33 @@ int32_t workgroups(const pa_kv_pool *p) {
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(kComputeUnits, u));
 }
 
+// KV heads per workgroup when the sequences' block counts differ (the kernel
+// sees the lengths, the host does not): the widest chunk, unless the caller
+// fixed the chunk.  With lengths that differ, ranges cut across (sequence,
+// chunk) pairs whatever the chunk, and fewer, longer pieces win: batch 32,
+// 8 KV heads, lengths uniform in [128, 8192]: 134 us at 1 head per
+// workgroup, 108 us at 4; the 64-sequence mix of up to 16K tokens: 331 us
+// at 2, 321 us at 4.
+int32_t heads_per_workgroup_varied(const pa_kv_pool *p) {
+  if (p->heads_override > 0) return p->heads_override;
+  return max_heads_per_workgroup(p->num_kv_heads);
+}
+
 struct Layout {
-  int32_t nwg, hc, chunks;
+  int32_t nwg, hc, chunks, hc_var;
   size_t ml_bytes, acc_offset, total;
 };
 
 // Workspace: two partial records per workgroup (the pieces its range starts
-// and ends with), each hc * G query heads of (max, sum) and d floats.
+// and ends with), each hc * G query heads of (max, sum) and d floats, for
+// the wider of the two head chunks the kernel may use.
 Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
   Layout L{};
   L.hc = heads_per_workgroup(p);
   L.chunks = p->num_kv_heads / L.hc;
+  L.hc_var = heads_per_workgroup_varied(p);
   L.nwg = workgroups(p);
-  const int32_t hcg = L.hc * (hq / p->num_kv_heads);
+  const int32_t hcg = std::max(L.hc, L.hc_var) * (hq / p->num_kv_heads);
   // one workgroup never splits a (sequence, chunk): no partials to keep
   const size_t recs = L.nwg > 1 ? (size_t)L.nwg * 2 * hcg : 0;
   L.ml_bytes = recs * sizeof(float2);
@@ -226,6 +240,7 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   a.nwg = L.nwg;
   a.hc = L.hc;
   a.chunks = L.chunks;
+  a.hc_var = L.hc_var;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.kv = kind_of(pool->kv_dtype);
 

@@ -55,8 +55,10 @@ struct LaunchArgs {
   uint32_t *counters;       // [batch][chunks] arrival counters, zero between runs
   int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx;
   int32_t nwg;              // workgroups (equal ranges of the work)
-  int32_t hc;               // KV heads per workgroup (divides hkv and kWaves)
+  int32_t hc;               // KV heads per workgroup when every sequence has the
+                            // block count of max_ctx (divides hkv and kWaves)
   int32_t chunks;           // hkv / hc
+  int32_t hc_var;           // KV heads per workgroup otherwise (>= hc)
   float scale_log2e;        // softmax scale * log2(e)
   int kv;                   // KvKind
 };

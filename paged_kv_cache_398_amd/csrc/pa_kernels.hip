@@ -13,7 +13,10 @@
 //  - The work is counted in units (one 16-token block of one (sequence,
 //    chunk of hc adjacent KV heads) pair) and split into equal contiguous
 //    ranges, one per workgroup of kWaves waves, whatever the mix of context
-//    lengths.  A range is cut into pieces at pair boundaries.
+//    lengths.  A range is cut into pieces at pair boundaries.  hc is the
+//    host's choice for a batch whose sequences all have the block count of
+//    max_context_len, and the widest chunk otherwise (ranges then cut
+//    across pairs anyway, and fewer, longer pieces stream faster).
 //  - In a piece, wave w works on head w % hc of the chunk and takes every
 //    (kWaves/hc)-th block.  A wave holds a whole block of its head in
 //    registers: each token row is split over LPT lanes, 64/LPT tokens per
@@ -511,10 +514,9 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   // wave index, known wave-uniform: everything derived from it stays scalar
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwg = gridDim.x, wgi = blockIdx.x;
-  const int hc = a.hc, chunks = a.chunks;
-  const int nph = kWaves / hc;  // phases: waves sharing a head
-  const int hl = w % hc, ph = w / hc;
-  const int hcg = hc * G;       // query heads of a chunk
+  // head chunk of an equal-length batch (a.hc): the speculation below uses it
+  const int hc0 = a.hc;
+  const int nph0 = kWaves / hc0, hl0 = w % hc0, ph0 = w / hc0;
 
   auto seq_len = [&](int b) { return min(max(a.ctx[b], 0), a.max_ctx); };
   auto seq_blocks = [&](int b) { return (seq_len(b) + kBlock - 1) / kBlock; };
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   // entries are loaded now, in flight together with the lengths the split
   // below needs, and used if the lengths confirm the guess.
   const int nbm = (a.max_ctx + kBlock - 1) / kBlock;
-  const long long Ug = (long long)a.batch * chunks * nbm;
+  const long long Ug = (long long)a.batch * a.chunks * nbm;
   Query<KV, D, G> qry_g;
   int tv_g = -1;
   {
@@ -535,39 +537,54 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     const long long u0g = wgi * per_g + min((long long)wgi, rem_g);
     const long long u1g = u0g + per_g + (wgi < rem_g ? 1 : 0);
     if (u0g < u1g) {
-      const int bg = (int)(u0g / ((long long)chunks * nbm));
-      const long long off = u0g - (long long)bg * chunks * nbm;
+      const int bg = (int)(u0g / ((long long)a.chunks * nbm));
+      const long long off = u0g - (long long)bg * a.chunks * nbm;
       const int cg = (int)(off / nbm), lo = (int)(off % nbm);
-      const int hi = (int)min((long long)nbm, u1g - (long long)bg * chunks * nbm - (long long)cg * nbm);
-      load_query<KV, D, G>(a, bg, cg * hc + hl, qry_g);
-      tv_g = load_table(a, bg, lo, ph, nph, 0,
-                        wave_blocks(lo * kBlock, min(a.max_ctx, hi * kBlock), ph, nph));
+      const int hi = (int)min((long long)nbm, u1g - (long long)bg * a.chunks * nbm - (long long)cg * nbm);
+      load_query<KV, D, G>(a, bg, cg * hc0 + hl0, qry_g);
+      tv_g = load_table(a, bg, lo, ph0, nph0, 0,
+                        wave_blocks(lo * kBlock, min(a.max_ctx, hi * kBlock), ph0, nph0));
     }
   }
 
-  // ---- total units U, this workgroup's range [u0, u1), and the sequence
-  // holding u0.  Up to kThreads sequences: one block-wide scan of the
-  // per-sequence units gives all three.  More: a sum, then a chunked scan.
+  // ---- total blocks TB, from which the head chunk, the total units
+  // U = TB * chunks, this workgroup's range [u0, u1) and the sequence holding
+  // u0.  Up to kThreads sequences: one block-wide scan of the per-sequence
+  // blocks gives all of them.  More: a sum, then a chunked scan below.
   if (tid == 0) s_first[0] = -1;
-  long long U;
+  long long TB, incl_b = 0;
+  int my_len = 0;
   if (small_batch) {
-    const int len = tid < a.batch ? seq_len(tid) : 0;
-    s_len[tid] = len;
-    const long long ub = (long long)((len + kBlock - 1) / kBlock) * chunks;
-    const long long incl = block_scan(ub, s_scan, &U);
+    my_len = tid < a.batch ? seq_len(tid) : 0;
+    s_len[tid] = my_len;
+    incl_b = block_scan((my_len + kBlock - 1) / kBlock, s_scan, &TB);
+  } else {
+    long long t = 0;
+    for (int b = tid; b < a.batch; b += kThreads) t += seq_blocks(b);
+    TB = block_sum(t, s_scan);
+  }
+  // The head chunk: a.hc when every sequence has max_ctx's block count (the
+  // equal-length batch the host sized it for), else a.hc_var.  No sequence
+  // has more blocks than max_ctx, so that is exactly TB == batch * nbm.
+  const bool full = __builtin_amdgcn_readfirstlane((int)(TB == (long long)a.batch * nbm)) != 0;
+  const int hc = full ? a.hc : a.hc_var;
+  const int chunks = a.hkv / hc;
+  const int nph = kWaves / hc;  // phases: waves sharing a head
+  const int hl = w % hc, ph = w / hc;
+  const int hcg = hc * G;       // query heads of a chunk
+  const long long U = TB * chunks;
+  if (small_batch) {
+    const long long ub = (long long)((my_len + kBlock - 1) / kBlock) * chunks;
+    const long long incl = incl_b * chunks;
     if (ub > 0) {
       const long long per = U / nwg, rem = U % nwg;
       const long long u0 = wgi * per + min((long long)wgi, rem);
       if (incl - ub <= u0 && u0 < incl) {
         s_first[0] = tid;
         s_first[1] = incl - ub;
-        s_first[2] = len;
+        s_first[2] = my_len;
       }
     }
-  } else {
-    long long t = 0;
-    for (int b = tid; b < a.batch; b += kThreads) t += seq_blocks(b);
-    U = block_sum(t, s_scan) * chunks;
   }
   const long long per = U / nwg, rem = U % nwg;
   auto range_start = [&](long long wg) { return wg * per + min(wg, rem); };
@@ -639,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     // the guess holds when every sequence has max_ctx tokens' worth of
     // blocks and this one exactly max_ctx tokens: then the first piece is
     // the guessed one, same blocks and same tail
-    if (first_piece && U == Ug && n == a.max_ctx) {
+    if (first_piece && full && U == Ug && n == a.max_ctx) {
       attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qry_g, tv_g, s_acc, s_m, s_l);
     } else {
       Query<KV, D, G> qry;

@@ -194,6 +194,26 @@ def test_auto_launch_shape():
     assert expected_shape(2, 2, 100) == (2, 7) or expected_shape(2, 2, 100)[1] <= 14
 
 
+def test_workspace_covers_the_widest_chunk():
+    # 8 KV heads, batch 32, 4096 tokens: chunk 1 when the block counts are
+    # equal, 4 (the widest) when they differ; records sized for 4
+    h = pa.pa_kv_pool_create(8192, 16, 8, 128, "bf16", K, V)
+    try:
+        pa.pa_block_table_set(h, TBL, CTX, 32, 256, 4096)
+        assert pa.pa_decode_heads_per_workgroup(h) == 1
+        assert pa.pa_decode_workgroups(h) == 256
+        recs = 256 * 2 * 4 * 4  # two records per workgroup, 4 heads x G 4 each
+        ml = (recs * 8 + 255) // 256 * 256
+        assert pa.pa_decode_workspace_bytes(h, 32) == ml + recs * 128 * 4
+        # an override fixes the chunk for both cases
+        pa.pa_decode_set_heads_per_workgroup(h, 1)
+        recs = 256 * 2 * 1 * 4
+        ml = (recs * 8 + 255) // 256 * 256
+        assert pa.pa_decode_workspace_bytes(h, 32) == ml + recs * 128 * 4
+    finally:
+        pa.pa_kv_pool_destroy(h)
+
+
 def test_heads_override(pool):
     pa.pa_block_table_set(pool, TBL, CTX, 3, 64, 1000)
     assert _status(pa.pa_decode_set_heads_per_workgroup, pool, 3) == pa.binding.PA_ERR_SHAPE

@@ -88,6 +88,30 @@ def test_placed_pools(name):
     assert err <= TOL[s.kv_dtype]
 
 
+@pytest.mark.parametrize("case", ["equal_blocks", "one_short", "uniform"])
+def test_head_chunk_from_lengths(case):
+    """The kernel takes the host's head chunk when every sequence has the
+    block count of max_context_len and the widest one otherwise: both sides
+    of that choice at the Llama-3-8B shape, every sequence against the oracle."""
+    base = NAMED_SPECS["llama3_8b_b32_ctx4k"]
+    rng = np.random.default_rng(3981)
+    if case == "equal_blocks":   # 256 blocks each, ragged last blocks
+        lens = tuple(int(x) for x in rng.integers(4081, 4097, size=32))
+        lens = (4096,) + lens[1:]
+    elif case == "one_short":    # one sequence a block shorter
+        lens = (4096,) * 31 + (4080,)
+    else:                        # lengths uniform in [128, 4096]
+        lens = tuple(int(x) for x in rng.integers(128, 4097, size=32))
+    spec = dataclasses.replace(base, name=f"chunk_choice_{case}", context_lens=lens)
+    say(f"[parity] head chunk from lengths, {case}: generating")
+    inp = make_inputs(spec)
+    got = gpu_decode(inp)
+    assert np.isfinite(got).all()
+    err = max_err(got, oracle_decode(inp))
+    say(f"[parity] head chunk from lengths, {case}: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # small shapes: several blocks and partitions, ragged tails, every build
 
