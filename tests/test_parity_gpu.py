@@ -112,6 +112,28 @@ def test_head_chunk_from_lengths(case):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("case", ["varied", "equal_blocks"])
+def test_large_batch(case):
+    """More sequences than threads in a workgroup (256): the kernel's
+    block-count sum and chunked scan instead of the single scan."""
+    rng = np.random.default_rng(3982)
+    if case == "varied":      # 600 sequences, empty ones included
+        lens = tuple(int(x) for x in rng.integers(0, 301, size=600))
+    else:                     # 520 sequences of 10 blocks, ragged last blocks
+        lens = (160,) + tuple(int(x) for x in rng.integers(145, 161, size=519))
+    spec = Spec(name=f"large_batch_{case}", batch=len(lens), num_q_heads=8, num_kv_heads=2,
+                head_dim=64, kv_dtype="bf16", q_dtype="bf16", seed=3983, context_lens=lens)
+    say(f"[parity] large batch, {case}: {len(lens)} sequences")
+    inp = make_inputs(spec)
+    got = gpu_decode(inp)
+    assert np.isfinite(got).all()
+    err = max_err(got, oracle_decode(inp))
+    say(f"[parity] large batch, {case}: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    for b in np.flatnonzero(np.asarray(lens) == 0):
+        assert not got[b].any()
+
+
 # ---------------------------------------------------------------------------
 # small shapes: several blocks and partitions, ragged tails, every build
 
