@@ -418,14 +418,20 @@ constexpr int phase_tiles() { return D == 64 ? kWT : 1; }
 
 template <int D>
 struct WideCfg {
-  // LDS row stride (bytes): 64 B of padding per row.  Rows read together
-  // then start on different banks; measured on the prefill chunk, 32 or 64 B
-  // of padding ran 5-10% faster than 16 B.
-  static constexpr int RS = D * 2 + 64;
+  // LDS row strides (bytes), one per region, each making its reads
+  // conflict-free: a K operand read takes 16 B of one row per lane, lanes
+  // on consecutive rows, so K rows are 16 B apart modulo 128 (8 lanes then
+  // cover the 32 banks once); a transposing V read takes 8 B from each of
+  // 4 rows x 4 lanes, 32 contiguous bytes per row, so V rows are 32 B apart
+  // modulo 128.  (One stride of 64 B padding for both: the K reads 4-way
+  // and the V reads 2-way bank conflicts, conflict cycles 44% of the LDS
+  // active cycles in the counters.)
+  static constexpr int RSK = D * 2 + 16;
+  static constexpr int RSV = D * 2 + 32;
   static constexpr int ROWCH = D / 8;                  // 16-byte chunks per token row
   static constexpr int NCH = (kSR * ROWCH + kWThreads - 1) / kWThreads;  // chunks per thread per stage (K, and V)
   static constexpr bool ALL = kSR * ROWCH % kWThreads == 0;             // every thread has NCH chunks
-  static constexpr int STAGE = 2 * kSR * RS;           // one stage: kSR K rows, then kSR V rows
+  static constexpr int STAGE = kSR * (RSK + RSV);      // one stage: kSR K rows, then kSR V rows
 };
 
 template <int D, int G>
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   using C = ChunkCfg<D>;
   using WC = WideCfg<D>;
   constexpr int KM = C::KM, EV = C::EV;
-  constexpr int RS = WC::RS, NCH = WC::NCH, ROWCH = WC::ROWCH;
+  constexpr int RSK = WC::RSK, RSV = WC::RSV, NCH = WC::NCH, ROWCH = WC::ROWCH;
   constexpr int kPH = phase_tiles<D>();
   static_assert(kWT % kPH == 0, "whole phases");
   constexpr bool ALL = WC::ALL;
@@ -543,8 +549,8 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
         const int ci = tid + kWThreads * i;
         if (!ALL && ci >= kSR * ROWCH) break;
         const int row = ci / ROWCH, col = ci % ROWCH;
-        *reinterpret_cast<uint4 *>(base + row * RS + col * 16) = sk[i];
-        *reinterpret_cast<uint4 *>(base + (kSR + row) * RS + col * 16) = sv[i];
+        *reinterpret_cast<uint4 *>(base + row * RSK + col * 16) = sk[i];
+        *reinterpret_cast<uint4 *>(base + kSR * RSK + row * RSV + col * 16) = sv[i];
       }
       return;
     }
@@ -555,9 +561,9 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       const int row = ci / ROWCH, col = ci % ROWCH;
       const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
                                                         // whole vector would go through memory
-      *reinterpret_cast<uint4 *>(base + row * RS + col * 16) =
+      *reinterpret_cast<uint4 *>(base + row * RSK + col * 16) =
           make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk);
-      *reinterpret_cast<uint4 *>(base + (kSR + row) * RS + col * 16) =
+      *reinterpret_cast<uint4 *>(base + kSR * RSK + row * RSV + col * 16) =
           make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk);
     }
   };
@@ -569,15 +575,15 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     ok[0] = (unsigned)block_id(blk0) < (unsigned)a.num_blocks;
     ok[1] = (unsigned)block_id(blk0 + 1) < (unsigned)a.num_blocks;
     const bool full = ok[0] && ok[1] && (blk0 + 2) * kTok - 1 <= pfirst;
-    const char *lk = s_kv + st * WC::STAGE + r0s * RS;
-    const char *lv = lk + kSR * RS;
+    const char *lk = s_kv + st * WC::STAGE + r0s * RSK;
+    const char *lv = s_kv + st * WC::STAGE + kSR * RSK + r0s * RSV;
     // A operands of S^T: token c of block hb, dims 32m + 8q .. +7
     uint4 kop[2][KM];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int m = 0; m < KM; ++m)
-        kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + (16 * hb + c) * RS + (32 * m + 8 * q) * 2);
+        kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + (16 * hb + c) * RSK + (32 * m + 8 * q) * 2);
     // B operands of O = P V, one per 16 dims (slab m): lane (n = c, q)
     // needs V[token 4q + e of block hb][dim 16m + n] for e = 0..3, hb = 0, 1.
     // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of
@@ -591,7 +597,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
         h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RS + (16 * m + 4 * (c & 3)) * 2));
+            (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
       vb[m] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // the tiles in groups of kPH: all score products of a group first, then
