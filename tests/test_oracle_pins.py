@@ -230,6 +230,76 @@ _SMALL = Spec(name="pin_small", batch=4, num_q_heads=8, num_kv_heads=2, head_dim
               pool_blocks=20)
 
 
+def _online_state(qh, K, V, scale, tile):
+    """One head's (running max m, running sum l, unnormalised output acc)
+    over tokens K, V ([n, d]) taken `tile` at a time: the FlashAttention
+    recurrence of the "LLM 推理优化" notes, section 三, with the standard
+    log-sum-exp (section 三's printed one is garbled).  Base-e throughout."""
+    m, l, acc = -math.inf, 0.0, np.zeros(K.shape[1])
+    for t0 in range(0, K.shape[0], tile):
+        s = scale * (K[t0:t0 + tile] @ qh)
+        m_new = max(m, float(s.max()))
+        c = 0.0 if m == -math.inf else math.exp(m - m_new)
+        p = np.exp(s - m_new)
+        l = c * l + float(p.sum())
+        acc = c * acc + p @ V[t0:t0 + tile]
+        m = m_new
+    return m, l, acc
+
+
+def _recurrence_case(seed):
+    """Four sequences of GQA tokens (Hq 4, Hkv 2, d 16) placed in a paged pool."""
+    rng = _rng(seed)
+    lens = [1, 7, 37, 100]
+    Hq, Hkv, d = 4, 2, 16
+    seqs = [(rng.standard_normal((n, Hkv, d)), rng.standard_normal((n, Hkv, d))) for n in lens]
+    q = rng.standard_normal((len(lens), Hq, d))
+    pool = AppendOnlyPool(sum((n + 15) // 16 for n in lens) + 3, Hkv, d, rng)
+    for t in range(max(lens)):
+        for b, (K, V) in enumerate(seqs):
+            if t < lens[b]:
+                pool.append(b, K[t], V[t])
+    scale = 1.0 / math.sqrt(d)
+    got = _oracle(q, pool.k, pool.v, pool.table(len(lens)), lens, scale)
+    return q, seqs, scale, got, Hq // Hkv
+
+
+def pin_online_recurrence_at_several_tile_sizes():
+    """The one-pass recurrence (rescale the partial sums whenever the max
+    rises) reaches the two-pass definition: at tiles of 1, 3, 16, 17 and
+    whole sequences it matches the oracle to 1e-12."""
+    q, seqs, scale, got, G = _recurrence_case(51)
+    for b, (K, V) in enumerate(seqs):
+        for h in range(q.shape[1]):
+            g = h // G
+            for tile in (1, 3, 16, 17, K.shape[0]):
+                m, l, acc = _online_state(q[b, h], K[:, g], V[:, g], scale, tile)
+                np.testing.assert_allclose(acc / l, got[b, h], rtol=0, atol=1e-12)
+
+
+def pin_split_parts_merge_to_the_whole():
+    """A sequence cut into parts (some empty), each reduced to (m, l, acc) on
+    its own, then merged with weights exp(m_p - M), M = max m_p (an empty
+    part weighs 0): out = sum w_p acc_p / sum w_p l_p -- the combination of
+    split sequences -- matches the oracle to 1e-12."""
+    q, seqs, scale, got, G = _recurrence_case(52)
+    rng = _rng(53)
+    for b, (K, V) in enumerate(seqs):
+        n = K.shape[0]
+        for _ in range(3):
+            cuts = sorted(int(x) for x in rng.integers(0, n + 1, size=3))
+            bounds = [0] + cuts + [n]
+            for h in range(q.shape[1]):
+                g = h // G
+                parts = [_online_state(q[b, h], K[lo:hi, g], V[lo:hi, g], scale, 5)
+                         for lo, hi in zip(bounds[:-1], bounds[1:])]
+                M = max(m for m, _, _ in parts)
+                w = [0.0 if m == -math.inf else math.exp(m - M) for m, _, _ in parts]
+                num = sum(wi * acc for wi, (_, _, acc) in zip(w, parts))
+                den = sum(wi * l for wi, (_, l, _) in zip(w, parts))
+                np.testing.assert_allclose(num / den, got[b, h], rtol=0, atol=1e-12)
+
+
 def pin_block_relabelling_is_bit_exact():
     inp = make_inputs(_SMALL)
     base = _oracle(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens,
