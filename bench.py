@@ -354,7 +354,7 @@ def main():
                          "(reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
