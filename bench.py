@@ -59,16 +59,115 @@ def kv_bytes(inp):
     return inp.unique_tokens * per_token
 
 
-def stored_traffic():
-    """HBM bytes per launch from committed counter runs, if still current."""
+def stored_traffic(workload):
+    """HBM bytes per launch of the attention kernel on ``workload`` from the
+    committed counter runs, if taken on that workload with the current
+    kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_sha():
+    if t.get("kernel_source_sha256") != kernel_source_sha() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
+
+
+def roofline_hbm(nbytes, kernel_s, kernel="attention_kernel", traffic=None):
+    a = nbytes / kernel_s / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "kernel_us": round(kernel_s * 1e6, 2)}
+
+
+def decode_leg(name, steps, warmup, layers=1, separate=False, main_inp=None):
+    """Time pa_decode_run / pa_decode_fp8_run on a named workload.
+
+    ``layers`` KV pools are cycled (so that no step finds its KV in the
+    256 MB Infinity Cache left by the previous one), each warmed by one run
+    first; then ``warmup`` untimed and ``steps`` timed back-to-back steps.
+    Returned: wall clock per step over the timed steps, and the attention
+    kernel's average duration from the library's HIP events around the
+    kernel on the steps that use pool 0.  Pools come from ``main_inp`` (host
+    arrays) when given, else are drawn on the GPU (make_device_workload).
+    ``separate``: K and V as two allocations instead of the recommended
+    one-buffer placement (pa_kv_pool_placement)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_398_amd as pa
+    from workloads import make_device_workload, named_spec
+    from workloads.device import to_device
+
+    s = named_spec(name)
+    w = to_device(main_inp) if main_inp is not None else make_device_workload(s)
+    n_blocks = int(w.k_pool.shape[0])
+    ctx_host = main_inp.context_lens if main_inp is not None else w.ctx_host
+    max_ctx = int(ctx_host.max())
+    pools = []
+    for r in range(layers):
+        if separate:
+            k, v = torch.empty_like(w.k_pool), torch.empty_like(w.v_pool)
+        else:
+            k, v = pa.allocate_kv_pools(n_blocks, s.num_kv_heads, s.head_dim, s.kv_dtype)
+        k.copy_(w.k_pool.view(k.dtype))
+        v.copy_(w.v_pool.view(v.dtype))
+        ks = None if w.k_scale is None else (w.k_scale if r == 0 else w.k_scale.clone())
+        vs = None if w.v_scale is None else (w.v_scale if r == 0 else w.v_scale.clone())
+        p = pa.PagedKVPool(k, v, s.kv_dtype, ks, vs)
+        p.set_block_table(w.block_table, w.context_lens, max_ctx)
+        pools.append(p)
+    q = w.q
+    scale = float(main_inp.scale if main_inp is not None else w.scale)
+    ws = pools[0].new_workspace(s.num_q_heads)
+    out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    R = len(pools)
+
+    def step(i):
+        pools[i % R].decode(q, out, ws, scale=scale)
+
+    for i in range(R + warmup):  # every pool once, then the warm-up steps
+        step(i)
+    torch.cuda.synchronize()
+    n_prof = (steps + R - 1) // R
+    pa.pa_profile_enable(pools[0].handle, n_prof)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = pa.pa_profile_read(pools[0].handle, n_prof)
+    pa.pa_profile_enable(pools[0].handle, 0)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError(f"non-finite output ({name})")
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[s.kv_dtype]
+    shared = (s.shared_prefix_seqs - 1) * s.shared_prefix_tokens if s.shared_prefix_seqs > 1 else 0
+    unique = int(ctx_host.astype(np.int64).sum()) - shared
+    per_token = s.num_kv_heads * s.head_dim * 2 * eb + (s.num_kv_heads * 2 * 4 if eb == 1 else 0)
+    nbytes = unique * per_token
+    sec = (t1 - t0) / steps
+    kern = statistics.fmean(kern_ms) * 1e-3
+    res = {
+        "workload": name, "kv_dtype": s.kv_dtype, "batch": s.batch,
+        "max_context_tokens": max_ctx, "kv_bytes_per_step": nbytes,
+        "steps": steps, "layers_cycled": R, "us_per_step": round(sec * 1e6, 2),
+        "tb_s": round(nbytes / sec / 1e12, 4),
+        "pct_of_hbm_peak": round(100 * nbytes / sec / 1e9 / HBM_PEAK_GBS, 2),
+        "workgroups": pools[0].workgroups(),
+        "kv_heads_per_workgroup_equal_lengths": pools[0].heads_per_workgroup(),
+        "kv_placement": "two separate allocations" if separate else
+                        "one buffer, V at a 2 KiB boundary + 256 B (pa_kv_pool_placement)",
+        "roofline": roofline_hbm(nbytes, kern, traffic=stored_traffic(name) if not separate
+                                 else None),
+        "kernel_event_pairs": len(kern_ms),
+    }
+    log(f"{name}{' (separate K/V)' if separate else ''}: {sec * 1e6:.1f} us/step, "
+        f"{res['tb_s']:.3f} TB/s; kernel {kern * 1e6:.1f} us "
+        f"({100 * res['roofline']['frac']:.1f}% of HBM peak)")
+    for p in pools:
+        p.close()
+    return res
 
 
 def cpu_baseline(inp, seconds):
@@ -347,6 +446,9 @@ def main():
                     help="timed steps of each INT8/INT4 decode leg (0: skip)")
     ap.add_argument("--bm-iters", type=int, default=20,
                     help="append rounds of the block-manager leg (0: skip)")
+    ap.add_argument("--decode-steps", type=int, default=20,
+                    help="timed steps of each other named decode workload, and of the "
+                         "main workload with K and V in separate allocations (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -391,14 +493,16 @@ def main():
     nwg = pools[0].workgroups()
     hc = pools[0].heads_per_workgroup()
     ws_bytes = pools[0].workspace_bytes(s.num_q_heads)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = pools[0].new_workspace(s.num_q_heads)
     out = torch.empty((s.batch, s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
     scale = float(inp.scale)
 
     def step(i):
-        pools[i % R].decode(dev.q, out, ws if ws_bytes else None, scale=scale)
+        pools[i % R].decode(dev.q, out, ws, scale=scale)
 
-    for i in range(args.warmup):
+    # every pool runs once before the warm-up steps, so that no first use of
+    # a pool falls inside the timed region whatever --warmup is
+    for i in range(R + args.warmup):
         step(i)
     torch.cuda.synchronize()
     # HIP events around the kernels of the steps that use pool 0 (every R-th
@@ -465,6 +569,17 @@ def main():
         append = {"us": round(us, 2), "bytes_written": written, "iters": args.append_iters,
                   "note": "pa_cache_append of one new token per sequence, back-to-back launches"}
         log(f"cache write: {us:.2f} us per launch")
+    # the other named decode workloads, and the main one with K and V in two
+    # separate allocations (the usual engine layout)
+    others = []
+    if args.decode_steps > 0:
+        others.append(decode_leg(s.name, args.decode_steps, args.warmup, layers=R,
+                                 separate=True, main_inp=inp))
+        for name in ("continuous_batch_b64", "long_ctx_b4_128k", "fp8_mha_b32_ctx8k"):
+            if name != s.name:
+                torch.cuda.empty_cache()
+                others.append(decode_leg(name, args.decode_steps, args.warmup))
+        torch.cuda.empty_cache()
     chunk = None
     if args.chunk_iters > 0:
         chunk = [chunk_leg(name, args.chunk_iters, inp, pools)
@@ -488,7 +603,7 @@ def main():
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(inp, args.cpu_seconds)
 
-    traffic = stored_traffic()
+    traffic = stored_traffic(s.name)
     res = {
         "metric": METRIC,
         "value": round(tbs, 4),
@@ -511,6 +626,7 @@ def main():
             "layers_cycled": R, "kv_heads_per_workgroup": hc,
             "kv_placement": "K and V pools of a layer in one buffer, V at a 2 KiB "
                             "boundary + 256 B (pa_kv_pool_placement)",
+            "untimed_runs_before_timing": R + args.warmup,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -529,6 +645,7 @@ def main():
             "note": "one step after reading 1 GiB elsewhere; event-timed step",
         },
         "cpu_baseline": cpu,
+        "decode_workloads": others,
         "cache_append": append,
         "chunk": chunk,
         "block_manager": block_mgr,

@@ -29,16 +29,13 @@
  *
  * Conventions shared by every call.
  *   - Pointers named "device" point to GPU memory of the current HIP device;
- *     the caller allocates, owns and frees all of them.  The library owns
- *     the host-side handle and one small device array per handle: arrival
- *     counters (4 bytes per sequence and head chunk), allocated and cleared
- *     on the first run that needs them (hipMalloc, so that first run waits
- *     for the device), grown when the batch grows, freed by
- *     pa_kv_pool_destroy.  Every run leaves them zero.
+ *     the caller allocates, owns and frees all of them, scratch memory
+ *     included (the decode workspace).  The library owns only host-side
+ *     handles: no entry point allocates or frees device memory.
  *   - Work is enqueued asynchronously on the caller's stream (a hipStream_t
  *     passed as void*; NULL is the default stream).  No call synchronises,
- *     except pa_block_table_validate.  Device buffers must stay valid until
- *     the enqueued work completes.
+ *     except the debugging aids pa_block_table_validate and pa_profile_read.
+ *     Device buffers must stay valid until the enqueued work completes.
  *   - Every call validates its arguments on the host before any HIP call
  *     and returns a pa_status.  On failure nothing is enqueued and
  *     pa_last_error() (thread-local) holds a one-line description.
@@ -47,9 +44,9 @@
  *     give undefined *values* in out, never an out-of-bounds access: the
  *     kernels clamp lengths to max_context_len and skip block ids outside
  *     [0, num_blocks).
- *   - A handle is not thread-safe, and runs on one handle must be ordered
- *     (one stream, or synchronised): they share its counters.  Distinct
- *     handles are independent.
+ *   - A handle is not thread-safe.  Runs that share a decode workspace must
+ *     be ordered (one stream, or synchronised).  Distinct handles with
+ *     distinct workspaces are independent.
  */
 #ifndef PA_H
 #define PA_H
@@ -63,6 +60,11 @@ extern "C" {
 
 /* Tokens per physical block (fixed). */
 #define PA_BLOCK_SIZE 16
+
+/* Bytes at the start of a decode workspace that hold arrival counters:
+ * zero before the first run (pa_decode_workspace_clear), left zero by every
+ * run.  One 32-bit counter for each of at most 65536 workgroups. */
+#define PA_DECODE_COUNTER_BYTES 262144
 
 typedef struct pa_kv_pool pa_kv_pool; /* opaque host-side handle */
 
@@ -351,17 +353,32 @@ pa_status pa_chunk_tiles(const pa_kv_pool *pool, int32_t num_q_heads, int32_t ma
  * The kernel's workgroups take equal shares of the batch's 16-token blocks
  * (whatever the mix of context lengths), so a sequence may be split
  * between two or more workgroups.  Each piece of a split sequence leaves a
- * running max, a running sum and an unnormalised output per query head,
- * combined exactly (log-sum-exp) by the workgroup that finishes last.  The
- * workspace holds two such records per workgroup, sized for the widest head
- * chunk a run may use; its size depends on the workgroup count, the head
- * chunks (pa_decode_workgroups, pa_decode_heads_per_workgroup) and
- * num_q_heads, not on the lengths.
- * *bytes receives the size (0 with a single workgroup).
+ * running max, a running sum and an unnormalised output per query head
+ * (the FlashAttention state of the qingdujian.com notes, section 三),
+ * combined exactly (log-sum-exp) by the workgroup that finishes last, which
+ * it finds with an arrival counter.  Layout: PA_DECODE_COUNTER_BYTES of
+ * counters (fixed size and place), then two records per workgroup sized for
+ * the widest head chunk a run may use; the size depends on the workgroup
+ * count, the head chunks (pa_decode_workgroups,
+ * pa_decode_heads_per_workgroup) and num_q_heads, not on the lengths.
+ * *bytes receives the size (0 with a single workgroup: nothing is split).
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_SHAPE.
  */
 pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads,
                                     size_t *bytes);
+
+/*
+ * pa_decode_workspace_clear -- prepare a decode workspace for its first run.
+ *
+ * Enqueues on `stream` a kernel that zeroes the counter region (the first
+ * min(workspace_bytes, PA_DECODE_COUNTER_BYTES) bytes).  Call it once after
+ * allocating a workspace (or zero the whole buffer any other way); every run
+ * leaves the counters zero again, so a workspace stays ready for runs of
+ * any shape that fit it.  Allocates nothing and does not wait.
+ * workspace: device, 256-byte aligned (NULL allowed when workspace_bytes is 0).
+ * Errors: PA_ERR_NULL, PA_ERR_WORKSPACE (misaligned), PA_ERR_HIP.
+ */
+pa_status pa_decode_workspace_clear(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_decode_run -- one decode step over an f32 or bf16 pool.
@@ -372,9 +389,10 @@ pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads,
  *   num_q_heads/num_kv_heads in {1, 2, 4, 8}.
  * scale: softmax scale, normally 1/sqrt(head_dim) (d7kj.com page, section 一).
  * out: device float32 [batch][num_q_heads][head_dim], written in full.
- * workspace: device, 256-byte aligned, at least pa_decode_workspace_bytes;
- *   its contents are scratch (no need to clear).  May be NULL when that
- *   size is 0.  Runs that overlap in time must not share a workspace.
+ * workspace: device, 256-byte aligned, at least pa_decode_workspace_bytes,
+ *   its counter region zero (pa_decode_workspace_clear once after
+ *   allocation; runs leave it zero); the rest is scratch.  May be NULL when
+ *   that size is 0.  Runs that overlap in time must not share a workspace.
  * stream: hipStream_t of the caller.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE (pool is FP8, or q_dtype
  *   does not match), PA_ERR_UNSUPPORTED (group size), PA_ERR_STATE (no

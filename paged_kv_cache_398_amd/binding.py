@@ -16,6 +16,7 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
 
 PA_BLOCK_SIZE = 16
+PA_DECODE_COUNTER_BYTES = 262144
 PA_DTYPE = {"f32": 0, "bf16": 1, "fp8_e4m3": 2, "int8_kivi": 3, "int4_kivi": 4}
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE = 0, 1, 2, 3
@@ -50,6 +51,7 @@ SIGNATURES = [
     ("pa_bm_table", _i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     ("pa_bm_stats", _i32, [_vp, _pi32, _pi32, _pi32]),
     ("pa_decode_workspace_bytes", _i32, [_vp, _i32, ctypes.POINTER(_sz)]),
+    ("pa_decode_workspace_clear", _i32, [_vp, _sz, _vp]),
     ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_set_workgroups", _i32, [_vp, _i32]),
@@ -262,6 +264,11 @@ def pa_decode_workspace_bytes(pool, num_q_heads) -> int:
     n = _sz()
     _check(load_library().pa_decode_workspace_bytes(pool, num_q_heads, ctypes.byref(n)))
     return n.value
+
+
+def pa_decode_workspace_clear(workspace, workspace_bytes, stream=None) -> None:
+    _check(load_library().pa_decode_workspace_clear(_ptr(workspace), workspace_bytes,
+                                                    _stream(stream)))
 
 
 def pa_decode_run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes,

@@ -8,6 +8,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -25,7 +27,7 @@ ARCH = "gfx950"
 # of them to VGPRs and back on every loop iteration, for the rarely taken
 # rescaling of the online softmax.  Only the MFMA kernels are affected.
 HIP_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
@@ -39,11 +41,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpa.so)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,7 +51,25 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source to an object (in parallel), then link libpa.so."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    obj_dir = tempfile.mkdtemp(prefix="pa_build_")
+    try:
+        inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+        objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc(), *HIP_FLAGS, *extra_flags, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB_PATH + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(obj_dir, ignore_errors=True)
     return LIB_PATH
 
 

@@ -3,8 +3,9 @@
 //
 // Every entry point validates on the host before touching the HIP runtime,
 // so argument errors are reported without a GPU.  Callers pass every data
-// buffer; the only device memory the library allocates is a handle's small
-// array of arrival counters (4 bytes per sequence and head chunk).
+// buffer and every scratch buffer; no entry point allocates or frees device
+// memory or waits for the device (pa_block_table_validate and
+// pa_profile_read, two debugging aids, wait).
 
 #include <hip/hip_runtime.h>
 
@@ -33,9 +34,6 @@ struct pa_kv_pool {
   int32_t batch = 0, max_blocks_per_seq = 0, max_context_len = 0;
   int32_t workgroups_override = 0;  // 0: automatic
   int32_t heads_override = 0;       // 0: automatic
-  // arrival counters of split (sequence, chunk) pairs: device, zero between runs
-  uint32_t *counters = nullptr;
-  size_t counter_capacity = 0;  // in counters
   // profiling
   int32_t prof_capacity = 0, prof_count = 0;
   std::vector<hipEvent_t> prof_events;  // 2 per run: before and after the kernel
@@ -138,13 +136,22 @@ int32_t heads_per_workgroup_varied(const pa_kv_pool *p) {
 
 struct Layout {
   int32_t nwg, hc, chunks, hc_var;
-  size_t ml_bytes, acc_offset, total;
+  size_t ml_offset, acc_offset, total;
 };
 
-// Workspace: two partial records per workgroup (the pieces its range starts
-// and ends with), each hc * G query heads of (max, sum) and d floats, for
-// the wider of the two head chunks the kernel may use.
+// Workspace, when a run may split pairs (more than one workgroup):
+//   [0, PA_DECODE_COUNTER_BYTES)  arrival counters, uint32 per workgroup
+//                                 (at most kMaxWorkgroups of them), zero
+//                                 before and after every run;
+//   then float2 ml[nwg][2][hcg]   (max, sum) of the two partial records of
+//                                 each workgroup (the pieces its range
+//                                 starts and ends with), and at a 256-byte
+//                                 boundary float acc[nwg][2][hcg][d], for
+//                                 hcg = query heads of the wider head chunk.
+// The counter region has a fixed size and place whatever the launch shape,
+// so one workspace, cleared once, serves runs of any shape.
 Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
+  static_assert(PA_DECODE_COUNTER_BYTES == 4 * kMaxWorkgroups, "one counter per workgroup");
   Layout L{};
   L.hc = heads_per_workgroup(p);
   L.chunks = p->num_kv_heads / L.hc;
@@ -153,8 +160,8 @@ Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
   const int32_t hcg = std::max(L.hc, L.hc_var) * (hq / p->num_kv_heads);
   // one workgroup never splits a (sequence, chunk): no partials to keep
   const size_t recs = L.nwg > 1 ? (size_t)L.nwg * 2 * hcg : 0;
-  L.ml_bytes = recs * sizeof(float2);
-  L.acc_offset = (L.ml_bytes + 255) & ~(size_t)255;
+  L.ml_offset = PA_DECODE_COUNTER_BYTES;
+  L.acc_offset = (L.ml_offset + recs * sizeof(float2) + 255) & ~(size_t)255;
   L.total = recs ? L.acc_offset + recs * p->head_dim * sizeof(float) : 0;
   return L;
 }
@@ -193,31 +200,10 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
     return fail(PA_ERR_SHAPE, "batch * num_q_heads too large");
   if (pool->batch == 0) return ok();
 
-  // ---- from here on HIP is used
+  // ---- from here on HIP is used (launches only: no allocation, no wait)
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  // Arrival counters of split (sequence, chunk) pairs: owned by the handle,
-  // zero between runs (the merging workgroup resets its counter).  Grown,
-  // and cleared by a kernel, only when the batch needs more of them.
-  const size_t ncnt = (size_t)pool->batch * L.chunks;
-  if (ncnt > pool->counter_capacity) {
-    // hipFree waits for the device, so no run still uses the old counters
-    if (pool->counters && (e = hipFree(pool->counters)) != hipSuccess)
-      return fail(PA_ERR_HIP, "hipFree(counters): %s", hipGetErrorString(e));
-    pool->counters = nullptr;
-    pool->counter_capacity = 0;
-    const size_t cap = std::max<size_t>(ncnt, 1024);
-    void *ptr = nullptr;
-    if ((e = hipMalloc(&ptr, cap * sizeof(uint32_t))) != hipSuccess)
-      return fail(PA_ERR_HIP, "hipMalloc(counters): %s", hipGetErrorString(e));
-    if ((e = pa::launch_zero(static_cast<uint32_t *>(ptr), cap, s)) != hipSuccess) {
-      (void)hipFree(ptr);
-      return fail(PA_ERR_HIP, "clearing the counters: %s", hipGetErrorString(e));
-    }
-    pool->counters = static_cast<uint32_t *>(ptr);
-    pool->counter_capacity = cap;
-  }
-
+  char *ws = static_cast<char *>(workspace);
   pa::LaunchArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
@@ -227,9 +213,9 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   a.table = pool->block_table;
   a.ctx = pool->context_lens;
   a.out = out;
-  a.ws_ml = static_cast<float2 *>(workspace);
-  a.ws_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.acc_offset);
-  a.counters = pool->counters;
+  a.counters = L.total ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+  a.ws_ml = L.total ? reinterpret_cast<float2 *>(ws + L.ml_offset) : nullptr;
+  a.ws_acc = L.total ? reinterpret_cast<float *>(ws + L.acc_offset) : nullptr;
   a.num_blocks = pool->num_blocks;
   a.hkv = pool->num_kv_heads;
   a.hq = hq;
@@ -364,7 +350,6 @@ pa_status pa_kv_pool_placement(int32_t num_blocks, int32_t num_kv_heads, int32_t
 void pa_kv_pool_destroy(pa_kv_pool *pool) {
   if (!pool) return;
   release_events(pool);
-  if (pool->counters) (void)hipFree(pool->counters);
   delete pool;
 }
 
@@ -424,6 +409,17 @@ pa_status pa_decode_workspace_bytes(const pa_kv_pool *pool, int32_t num_q_heads,
     return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 num_q_heads, pool->num_kv_heads);
   *bytes = workspace_layout(pool, num_q_heads).total;
+  return ok();
+}
+
+pa_status pa_decode_workspace_clear(void *workspace, size_t workspace_bytes, void *stream) {
+  if (workspace_bytes == 0) return ok();
+  if (!workspace) return fail(PA_ERR_NULL, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  const size_t words = std::min<size_t>(workspace_bytes, PA_DECODE_COUNTER_BYTES) / 4;
+  const hipError_t e =
+      pa::launch_zero(static_cast<uint32_t *>(workspace), words, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "clearing the workspace: %s", hipGetErrorString(e));
   return ok();
 }
 

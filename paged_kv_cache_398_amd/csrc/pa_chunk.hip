@@ -48,10 +48,14 @@
 //  - The row sums l come out of the matrix cores too: one more product per
 //    tile with A = all ones gives every lane the sum of its row's weights.
 //
-// Probabilities enter the PV product rounded to bf16 (relative error at
-// most 2^-9 each); the normaliser l sums the same rounded values, so the
-// output is a convex combination of V rows whose weights are off by at most
-// a relative 2^-8.  Positions past a row's own, and blocks or table entries
+// Probabilities enter the PV product as a sum of two bf16 values, hi (the
+// probability truncated to bf16) and lo (the remainder rounded to bf16):
+// two products per slab, hi + lo within a relative 2^-16 of the fp32
+// probability.  The normaliser l sums the same hi + lo, so the output is a
+// convex combination of V rows whose weights are off by at most a relative
+// 2^-15.  (One bf16 product, a relative 2^-9 per weight, gave errors up to
+// 2.8e-3 on contexts of a few tokens.)  Positions past a row's own, and
+// blocks or table entries
 // outside the pool, contribute exactly nothing: their scores are replaced by
 // -inf and the V rows of slots past the cached tokens by zeros (selects, not
 // products, so NaN garbage there cannot leak).
@@ -113,6 +117,22 @@ __device__ __forceinline__ float max8(const float (&x)[2][4]) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// p = hi + lo in bf16: hi is p truncated to bf16 (the upper half of its
+// bits, one byte permute per pair), the remainder p - hi is exact in fp32
+// and below 2^-7 p, and lo is that remainder rounded to the nearest bf16;
+// so hi + lo is within a relative 2^-16 of p.
+__device__ __forceinline__ void split_bf16(const float (&p)[8], bf16x8_t &hi, bf16x8_t &lo) {
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = __float_as_uint(p[2 * i]), b = __float_as_uint(p[2 * i + 1]);
+    h[i] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low), b (high)
+    lo[2 * i] = (__bf16)(p[2 * i] - __uint_as_float(a & 0xFFFF0000u));
+    lo[2 * i + 1] = (__bf16)(p[2 * i + 1] - __uint_as_float(b & 0xFFFF0000u));
+  }
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+}
 
 template <int N>
 __device__ __forceinline__ void load_dwords(const char *p, uint32_t *dst) {
@@ -297,19 +317,24 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
         for (int m = 0; m < EV; ++m) o[t][m] *= f;
       }
       const float nm = -mrun[t];
-      bf16x8_t pw;
+      float pf[8];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // a masked score (-inf) gives exactly 0
-          pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[hb][j] + nm);
+          pf[4 * hb + j] = __builtin_amdgcn_exp2f(x[hb][j] + nm);
         }
-      // the normaliser sums the same rounded weights, on the matrix cores
-      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pw, l4[t], 0, 0, 0);
+      bf16x8_t ph, pl;
+      split_bf16(pf, ph, pl);
+      // the normaliser sums the same weights (hi + lo), on the matrix cores
+      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph, l4[t], 0, 0, 0);
+      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl, l4[t], 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < EV; ++m)
-        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pw, o[t][m], 0, 0, 0);
+      for (int m = 0; m < EV; ++m) {
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], ph, o[t][m], 0, 0, 0);
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pl, o[t][m], 0, 0, 0);
+      }
     }
   };
   // ---- main loop: the wave's pairs w, w+4, ..., in chunks of 32 pairs
@@ -674,17 +699,22 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       for (int u = 0; u < kPH; ++u) {
         const int t = t0 + u;
         const float nm = -mrun[t];
-        bf16x8_t pw;
+        float pf[8];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pw[4 * hb + j] = (__bf16)__builtin_amdgcn_exp2f(x[u][hb][j] + nm);
-        // O = P V with A = P: lane (c, q)'s eight weights are row c's
-        // tokens 4q .. 4q+3 of both blocks, the same k order as vb
-        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pw, ones, l4[t], 0, 0, 0);
+          for (int j = 0; j < 4; ++j) pf[4 * hb + j] = __builtin_amdgcn_exp2f(x[u][hb][j] + nm);
+        bf16x8_t ph, pl;
+        split_bf16(pf, ph, pl);
+        // O = P V with A = P (hi, then lo): lane (c, q)'s eight weights are
+        // row c's tokens 4q .. 4q+3 of both blocks, the same k order as vb
+        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4[t], 0, 0, 0);
+        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4[t], 0, 0, 0);
 #pragma unroll
-        for (int m = 0; m < EV; ++m)
-          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pw, vb[m], o[t][m], 0, 0, 0);
+        for (int m = 0; m < EV; ++m) {
+          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb[m], o[t][m], 0, 0, 0);
+          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb[m], o[t][m], 0, 0, 0);
+        }
       }
     }
   };

@@ -7,10 +7,6 @@
 
 #include "pa.h"
 
-#ifndef PA_WAVES
-#define PA_WAVES 4
-#endif
-
 namespace pa {
 
 enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
@@ -19,8 +15,7 @@ enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 // partition of one sequence for a chunk of `hc` KV heads; wave w works on
 // head w % hc of the chunk and takes every (kWaves / hc)-th block of the
 // partition, so the workgroup as a whole streams whole physical blocks.
-constexpr int kWaves = PA_WAVES;
-static_assert(kWaves == 4 || kWaves == 8 || kWaves == 16, "4, 8 or 16 waves");
+constexpr int kWaves = 4;
 
 // Loads of cache bytes that one launch reads exactly once.  They carry the
 // non-temporal hint, so the caches do not keep lines that will not be read
@@ -52,7 +47,8 @@ struct LaunchArgs {
   float *out;               // [batch][hq][d]
   float2 *ws_ml;            // [nwg][2][hc*G] partial (running max, running sum)
   float *ws_acc;            // [nwg][2][hc*G][d] partial unnormalised output
-  uint32_t *counters;       // [batch][chunks] arrival counters, zero between runs
+  uint32_t *counters;       // [nwg] arrival counters (indexed by the first workgroup of
+                            // a split pair), zero before and after every run
   int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx;
   int32_t nwg;              // workgroups (equal ranges of the work)
   int32_t hc;               // KV heads per workgroup when every sequence has the
@@ -153,7 +149,9 @@ struct CopyArgs {
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
 
 // Enqueue a kernel that sets n 32-bit words to zero (a kernel rather than a
-// memset, so that a captured graph replays it faithfully).
+// memset, so that a captured graph replays it faithfully).  Only device
+// addresses (a caller's buffer, or a device symbol's address obtained with
+// hipGetSymbolAddress) may be passed.
 hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t stream);
 
 }  // namespace pa

@@ -54,19 +54,24 @@ namespace {
 constexpr int kBlock = 16;         // tokens per physical block
 constexpr int kThreads = kWaves * 64;
 constexpr float kTau = 8.0f;       // lag allowed to the running max (log2 units)
+// Start of the running max: the lowest finite float rather than -inf, so
+// that exp2(s - m) is 0 for a masked score (-inf) even before any valid
+// token was seen (a wave whose first blocks are all masked, e.g. block ids
+// outside the pool), never exp2(-inf - -inf) = NaN.  Any valid score raises
+// the max above it on its first block.
+constexpr float kNoMax = -3.402823466e38f;
 
 __host__ __device__ constexpr int elem_bytes(int kv) {
   return kv == KV_F32 ? 4 : (kv == KV_BF16 ? 2 : 1);
 }
 
-#ifndef PA_ACC_REGS
-#define PA_ACC_REGS 64
-#endif
+// Most fp32 output accumulators one lane keeps (G * D / LPT).
+constexpr int kAccRegs = 64;
 // Lanes per token row: as few as possible while keeping the per-lane output
-// accumulators (G * D / LPT floats) at PA_ACC_REGS registers or fewer, and
+// accumulators (G * D / LPT floats) at kAccRegs registers or fewer, and
 // each lane's slice of a row at 8 bytes or more.
 __host__ __device__ constexpr int lanes_per_token(int d, int g, int eb) {
-  int l = (g * d / 4 <= PA_ACC_REGS) ? 4 : ((g * d / 8 <= PA_ACC_REGS) ? 8 : 16);
+  int l = (g * d / 4 <= kAccRegs) ? 4 : ((g * d / 8 <= kAccRegs) ? 8 : 16);
   while (l > 4 && d * eb / l < 8) l /= 2;
   return l;
 }
@@ -305,7 +310,7 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -__builtin_huge_valf();
+    m[hh] = kNoMax;
     l[hh] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
@@ -445,11 +450,11 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
 }
 
 // Exact combination of weighted partial states: the running maxima of the
-// parts are aligned to their common maximum M (a part that saw no valid
-// token has m = -inf and weight 0).
-__device__ __forceinline__ float part_weight(float m, float M) {
-  return m == -__builtin_huge_valf() ? 0.f : fast_exp2(m - M);
-}
+// parts are aligned to their common maximum M.  A part that saw no valid
+// token has m = kNoMax and l = acc = 0: its weight is 0 next to any part
+// with a valid token (exp2(kNoMax - M) underflows) and, when no part has
+// one, every weight is 1 and the sum stays 0.
+__device__ __forceinline__ float part_weight(float m, float M) { return fast_exp2(m - M); }
 
 // Sum over the workgroup (int64), every thread gets the result.
 __device__ __forceinline__ long long block_sum(long long x, long long *scratch) {
@@ -499,7 +504,9 @@ __device__ __forceinline__ long long block_scan(long long x, long long *scratch,
 // normalised output is written.  A pair split over several ranges leaves a
 // partial state per piece in the workspace (record slot 0 for the piece a
 // range starts with, slot 1 for the piece it ends with); the last of those
-// pieces to finish, found with an arrival counter, merges them.
+// pieces to finish, found with an arrival counter, merges them.  The
+// counters (one per workgroup) are zero before the launch and the merging
+// workgroup sets its counter back to zero.
 
 template <int KV, int D, int G>
 __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
@@ -673,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     for (int idx = tid; idx < hcg * D; idx += kThreads) {
       const int r = idx / D, e = idx % D;  // r = hl * G + hh
       const int hh = r % G, hw = r / G;
-      float M = -__builtin_huge_valf();
+      float M = kNoMax;
       for (int v = 0; v < nph; ++v) M = fmaxf(M, s_m[v * hc + hw][hh]);
       float A = 0.f, L = 0.f;
       for (int v = 0; v < nph; ++v) {
@@ -696,8 +703,11 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
       // 0's device-scope release then covers them all.  The arrival that
       // completes the count acquires every earlier one (one release
       // sequence on the counter) and the barrier hands that on.
+      // The pair's counter is indexed by the first workgroup it touches: a
+      // range holds the first unit of at most one pair that runs past its
+      // end, so no two split pairs share a counter.
       const long long w_lo = range_of(seg_start), w_hi = range_of(seg_end - 1);
-      uint32_t *cnt = a.counters + (size_t)b * chunks + chunk;
+      uint32_t *cnt = a.counters + w_lo;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) {
@@ -719,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
         const float4 *acc4 = reinterpret_cast<const float4 *>(a.ws_acc);
         for (int idx = tid; idx < hcg * (D / 4); idx += kThreads) {
           const int r = idx / (D / 4), c4 = idx % (D / 4);
-          float M = -__builtin_huge_valf();
+          float M = kNoMax;
           for (int j = 0; j < np; ++j) M = fmaxf(M, a.ws_ml[rec_of(j) + r].x);
           float L = 0.f;
           float4 A = make_float4(0.f, 0.f, 0.f, 0.f);

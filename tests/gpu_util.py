@@ -24,7 +24,7 @@ def gpu_decode(inp, workgroups=0, heads=0, dev=None, out=None, workspace=None):
             pool.set_heads_per_workgroup(heads)
         if workspace is None:
             nbytes = pool.workspace_bytes(s.num_q_heads)
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+            workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
         if out is None:
             out = torch.full((s.batch, s.num_q_heads, s.head_dim), float("nan"),
                              dtype=torch.float32, device="cuda")
@@ -35,11 +35,31 @@ def gpu_decode(inp, workgroups=0, heads=0, dev=None, out=None, workspace=None):
         pool.close()
 
 
-def oracle_decode(inp, seqs=None):
-    return oracle.paged_decode_attention(
-        inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens, inp.scale,
-        kv_dtype=inp.spec.kv_dtype, q_dtype=inp.spec.q_dtype, k_scale=inp.k_scale,
-        v_scale=inp.v_scale, seqs=seqs)
+def oracle_decode(inp, seqs=None, threads=1):
+    """The oracle's output for ``seqs`` (all by default; other rows NaN).
+    ``threads`` > 1 computes the sequences concurrently, one oracle call per
+    sequence (numpy releases the GIL in its array work)."""
+    def one(sq):
+        return oracle.paged_decode_attention(
+            inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.context_lens, inp.scale,
+            kv_dtype=inp.spec.kv_dtype, q_dtype=inp.spec.q_dtype, k_scale=inp.k_scale,
+            v_scale=inp.v_scale, seqs=sq)
+
+    if threads <= 1:
+        return one(seqs)
+    from concurrent.futures import ThreadPoolExecutor
+    todo = list(range(inp.spec.batch)) if seqs is None else list(seqs)
+    out = np.full((inp.spec.batch, inp.spec.num_q_heads, inp.spec.head_dim), np.nan)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for b, r in zip(todo, ex.map(lambda b: one([b]), todo)):
+            out[b] = r[b]
+    return out
+
+
+def host_threads():
+    """Threads for the oracle: the host's CPUs, at most 16 (a GPU machine's share)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def max_err(got, want, seqs=None):

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 31
+    assert len(names) == 32
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -143,9 +143,7 @@ def test_workgroups_override_and_workspace_size(pool):
     assert pa.pa_decode_workgroups(pool) == 7
     hc = pa.pa_decode_heads_per_workgroup(pool)  # 2 KV heads, batch 3: split, hc 2
     assert hc == 2
-    recs = 7 * 2 * hc * (8 // 2)  # two records per workgroup, hc * G query heads each
-    ml = (recs * 8 + 255) // 256 * 256
-    assert pa.pa_decode_workspace_bytes(pool, 8) == ml + recs * 128 * 4
+    assert pa.pa_decode_workspace_bytes(pool, 8) == workspace_size(7, hc * (8 // 2), 128)
     # a single workgroup never splits a sequence: no workspace
     pa.pa_decode_set_workgroups(pool, 1)
     assert pa.pa_decode_workspace_bytes(pool, 8) == 0
@@ -157,7 +155,29 @@ def test_workgroups_override_and_workspace_size(pool):
     assert pa.pa_decode_workspace_bytes(pool, 8) == 0
 
 
-WAVES_PER_WG = 4  # PA_WAVES of the default build
+def workspace_size(nwg, hcg, d):
+    """The documented workspace layout, restated: the fixed counter region,
+    then (max, sum) float2 and, at a 256-byte boundary, d floats for each of
+    two records per workgroup of hcg query heads."""
+    recs = nwg * 2 * hcg
+    acc = (pa.PA_DECODE_COUNTER_BYTES + recs * 8 + 255) // 256 * 256
+    return acc + recs * d * 4
+
+
+def test_workspace_layout_constants():
+    assert pa.PA_DECODE_COUNTER_BYTES == 4 * 65536  # one counter per workgroup, at most 65536
+    text = open(HEADER).read()
+    assert "#define PA_DECODE_COUNTER_BYTES 262144" in text
+
+
+def test_workspace_clear_errors():
+    c = pa.pa_decode_workspace_clear
+    assert _status(c, None, 1024, 0) == pa.binding.PA_ERR_NULL
+    assert _status(c, WS + 16, 1024, 0) == pa.binding.PA_ERR_WORKSPACE
+    c(None, 0, 0)  # nothing to clear: no HIP call
+
+
+WAVES_PER_WG = 4  # waves per workgroup of the attention kernel
 CUS = 256
 
 
@@ -202,14 +222,11 @@ def test_workspace_covers_the_widest_chunk():
         pa.pa_block_table_set(h, TBL, CTX, 32, 256, 4096)
         assert pa.pa_decode_heads_per_workgroup(h) == 1
         assert pa.pa_decode_workgroups(h) == 256
-        recs = 256 * 2 * 4 * 4  # two records per workgroup, 4 heads x G 4 each
-        ml = (recs * 8 + 255) // 256 * 256
-        assert pa.pa_decode_workspace_bytes(h, 32) == ml + recs * 128 * 4
+        # two records per workgroup, 4 heads x G 4 each
+        assert pa.pa_decode_workspace_bytes(h, 32) == workspace_size(256, 16, 128)
         # an override fixes the chunk for both cases
         pa.pa_decode_set_heads_per_workgroup(h, 1)
-        recs = 256 * 2 * 1 * 4
-        ml = (recs * 8 + 255) // 256 * 256
-        assert pa.pa_decode_workspace_bytes(h, 32) == ml + recs * 128 * 4
+        assert pa.pa_decode_workspace_bytes(h, 32) == workspace_size(256, 4, 128)
     finally:
         pa.pa_kv_pool_destroy(h)
 

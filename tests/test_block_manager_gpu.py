@@ -131,7 +131,7 @@ class Engine:
                                                       dtype=np.float32)).to(torch.bfloat16)
         out = torch.empty((len(seqs), self.hq, self.d), dtype=torch.float32, device="cuda")
         wsb = self.pool.workspace_bytes(self.hq)
-        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
         self.pool.decode(q.cuda(), out, ws if wsb else None)
         torch.cuda.synchronize()
         got = out.cpu().numpy()

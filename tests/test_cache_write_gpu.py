@@ -155,17 +155,23 @@ def test_append_then_decode(kv, src):
     assert max_err(got, oracle_decode(after)) <= TOL[kv]
 
 
-def test_append_full_size_llama_step():
-    """The Llama-3-8B-shaped step: every sequence's new token at position
-    4095 is written as given (sampled sequences checked byte for byte)."""
+@pytest.mark.parametrize("name,src", [("llama3_8b_b32_ctx4k", "bf16"),
+                                      ("fp8_mha_b32_ctx8k", "f32"),
+                                      ("fp8_mha_b32_ctx8k", "bf16")])
+def test_append_full_size(name, src):
+    """The full-size workloads: every sequence's new token (position
+    ctx - 1) written into the 256 MiB bf16 pools, or quantised into the FP8
+    pools with their scales; every byte of the pools and scales equal to the
+    oracle's write (so also nothing else touched)."""
     from workloads import NAMED_SPECS
-    inp = make_inputs(NAMED_SPECS["llama3_8b_b32_ctx4k"])
+    inp = make_inputs(NAMED_SPECS[name])
     s = inp.spec
-    k_rows, v_rows = _new_rows(s.batch, s.num_kv_heads, s.head_dim, 91)
-    say("[append] llama3 full size")
-    dev = _run_append(inp, k_rows, v_rows, "bf16")
-    kp = _host(dev.k_pool)
-    for b in (0, 13, s.batch - 1):
-        t = int(inp.context_lens[b]) - 1
-        p = inp.block_table[b, t // 16]
-        assert np.array_equal(kp[p, t % 16], _bf16_bits(k_rows[b]))
+    k_rows, v_rows = _new_rows(s.batch, s.num_kv_heads, s.head_dim, 91, scale=2.0)
+    say(f"[append] {name} full size, src {src}")
+    dev = _run_append(inp, k_rows, v_rows, src)
+    want_k, want_v, want_ks, want_vs = _oracle_append(inp, k_rows, v_rows, src)
+    assert _same_bytes(_host(dev.k_pool), want_k)
+    assert _same_bytes(_host(dev.v_pool), want_v)
+    if s.kv_dtype == "fp8_e4m3":
+        assert _same_bytes(_host(dev.k_scale), want_ks)
+        assert _same_bytes(_host(dev.v_scale), want_vs)

@@ -1,13 +1,14 @@
 """GPU parity of the multi-token chunk attention (pa_chunk_run) with the oracle.
 
 Tolerance, from the kernel's arithmetic: q and K are bf16, so the products
-in the scores are exact and summed in fp32; the softmax weights enter the PV
-product rounded to bf16 (relative error at most 2^-9 each) and the
-normaliser sums the same rounded weights, so each output element is a convex
-combination of V values whose weights are off by at most a relative 2^-8:
-  |out - ref| <= 2^-8 * sum_t w_t |V_t| + 1e-4
+in the scores are exact and summed in fp32; each softmax weight enters the
+PV product as hi + lo, two bf16 values within a relative 2^-16 of it, and
+the normaliser sums the same hi + lo, so each output element is a convex
+combination of V values whose weights are off by at most a relative 2^-15:
+  |out - ref| <= 2^-15 * sum_t w_t |V_t| + 1e-4
 (the last term covers fp32 accumulation and the hardware exp2).  The bound
-is evaluated with the oracle itself, by running it on |V|.
+is evaluated with the oracle itself, by running it on |V|.  Every case must
+also meet the decode bar, 2e-3.
 """
 
 import dataclasses
@@ -61,8 +62,11 @@ def oracle_chunk(ci, seqs=None, abs_v=False):
                                         seqs=seqs)
 
 
+REL = 2.0 ** -15  # relative error of the weights the kernel uses
+
+
 def bound_of(ci, seqs=None):
-    return 2.0 ** -8 * oracle_chunk(ci, seqs, abs_v=True) + 1e-4
+    return REL * oracle_chunk(ci, seqs, abs_v=True) + 1e-4
 
 
 def rows_of(ci, seqs):
@@ -79,6 +83,8 @@ def assert_parity(ci, got, seqs=None):
     bad = err > bound[r]
     assert not bad.any(), (f"{bad.sum()} elements over the bound; max err {err.max():.3e}, "
                            f"worst excess {(err - bound[r]).max():.3e}")
+    # and the decode bar, which the derived bound does not imply for large |V|
+    assert not err.size or err.max() <= 2e-3, f"max err {err.max():.3e} > 2e-3"
     return float(err.max()) if err.size else 0.0
 
 
@@ -209,7 +215,7 @@ def test_chunk_single_rows_match_decode_path():
     try:
         pool.set_block_table(dev.block_table, dev.context_lens, base.max_context_len)
         ws_b = pool.workspace_bytes(32)
-        ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_b, 1), dtype=torch.uint8, device="cuda")
         pool.decode(q, out, ws if ws_b else None, scale=float(base.scale))
         torch.cuda.synchronize()
     finally:
@@ -227,28 +233,24 @@ def test_chunk_spec_verify_full_size():
     say(f"  max err {err:.2e}")
 
 
-def test_chunk_prefill_full_size_sampled():
-    """The 2048-row prefill chunk as the benchmark runs it; the oracle
-    computes sampled rows (a row at position p is the one-row chunk of a
-    sequence cut at p + 1 tokens)."""
+def test_chunk_prefill_full_size():
+    """The 2048-row prefill chunk as the benchmark runs it: every row of both
+    sequences against the oracle (one oracle call per sequence, for the
+    values and for the bound, run concurrently)."""
+    from concurrent.futures import ThreadPoolExecutor
     ci = make_chunk_inputs("prefill_chunk2k_b2_ctx4k")
     base = ci.base
     say(f"[chunk] prefill full size, rows={ci.total_rows}")
     got = gpu_chunk(ci)
     assert np.all(np.isfinite(got))
-    for b in range(base.spec.batch):
-        n, ctx = int(ci.q_lens[b]), int(base.context_lens[b])
-        for i in (0, 1, 15, 16, 17, 255, 1024, n - 2, n - 1):
-            r = int(ci.q_start[b]) + i
-            p = ctx - n + i
-            one = chunk_queries(base, [0] * base.spec.batch, 0)
-            one.q = ci.q[r:r + 1]
-            one.q_start = np.array([0] * (b + 1) + [1] * (base.spec.batch - b), np.int32)
-            one.q_lens = np.diff(one.q_start)
-            cut = base.context_lens.copy()
-            cut[b] = p + 1
-            one.base = type(base)(**{**base.__dict__, "context_lens": cut})
-            want = oracle_chunk(one, seqs=[b])[0]
-            bound = bound_of(one, seqs=[b])[0]
-            err = np.abs(got[r] - want)
-            assert np.all(err <= bound), (b, i, float(err.max()))
+    B = base.spec.batch
+    jobs = [(b, absv) for b in range(B) for absv in (False, True)]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        res = dict(zip(jobs, ex.map(lambda j: oracle_chunk(ci, [j[0]], abs_v=j[1]), jobs)))
+    for b in range(B):
+        r = rows_of(ci, [b])
+        want, bound = res[(b, False)][r], REL * res[(b, True)][r] + 1e-4
+        err = np.abs(got[r] - want)
+        say(f"  sequence {b}: max err {err.max():.2e}")
+        assert np.all(err <= bound), (b, float(err.max()))
+        assert err.max() <= 2e-3

@@ -11,6 +11,7 @@ from .synthetic import (  # noqa: F401
     Inputs,
     Spec,
     NAMED_SPECS,
+    make_device_workload,
     make_inputs,
     named_spec,
 )

@@ -174,9 +174,32 @@ def make_inputs(spec: Spec, poison: bool = False, seed: Optional[int] = None) ->
     block no table references (FP8: code 0x7F and a NaN scale).
     """
     s = spec
+    rng = np.random.Generator(np.random.PCG64(s.seed if seed is None else seed))
+    ctx, table, used, n_pool, out_ch, q = _layout_and_queries(s, rng)
+    B, hkv, d = s.batch, s.num_kv_heads, s.head_dim
+
+    # 4. values, continued: K pool, V pool
+    per_block = BLOCK_SIZE * hkv * d
+    chunk = max(1, (1 << 26) // per_block)
+    k_pool, k_scale = _draw_pool(rng, n_pool, hkv, d, s.kv_dtype, out_ch, s.outlier_gain, chunk)
+    v_pool, v_scale = _draw_pool(rng, n_pool, hkv, d, s.kv_dtype, out_ch, s.outlier_gain, chunk)
+
+    inp = Inputs(
+        spec=s, q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
+        block_table=table, context_lens=ctx.astype(np.int32),
+        scale=np.float32(1.0 / math.sqrt(d)), used_blocks=used,
+    )
+    if poison:
+        _poison(inp)
+    return inp
+
+
+def _layout_and_queries(s: Spec, rng):
+    """Steps 1-4 up to the pools: lengths, block table, outlier channels and
+    q.  Returns (ctx int64 [B], table int32 [B][max_blocks], used bool [N],
+    N, outlier channels or None, q)."""
     if s.num_q_heads % s.num_kv_heads:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
-    rng = np.random.Generator(np.random.PCG64(s.seed if seed is None else seed))
     B, hkv, d = s.batch, s.num_kv_heads, s.head_dim
 
     # 1. context lengths
@@ -231,22 +254,94 @@ def make_inputs(spec: Spec, poison: bool = False, seed: Optional[int] = None) ->
         n_out = int(round(s.outlier_frac * hkv * d))
         out_ch = np.sort(rng.choice(hkv * d, size=n_out, replace=False))
 
-    # 4. values: q, K pool, V pool
+    # 4. values: q (the pools follow)
     qf = rng.standard_normal((B, s.num_q_heads, d), dtype=np.float32)
     q = qf if s.q_dtype == "f32" else _to_bf16_bits(qf)
-    per_block = BLOCK_SIZE * hkv * d
-    chunk = max(1, (1 << 26) // per_block)
-    k_pool, k_scale = _draw_pool(rng, n_pool, hkv, d, s.kv_dtype, out_ch, s.outlier_gain, chunk)
-    v_pool, v_scale = _draw_pool(rng, n_pool, hkv, d, s.kv_dtype, out_ch, s.outlier_gain, chunk)
+    return ctx, table, used, n_pool, out_ch, q
 
-    inp = Inputs(
-        spec=s, q=q, k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
-        block_table=table, context_lens=ctx.astype(np.int32),
-        scale=np.float32(1.0 / math.sqrt(d)), used_blocks=used,
-    )
-    if poison:
-        _poison(inp)
-    return inp
+
+@dataclass
+class DeviceWorkload:
+    """A workload drawn for timing: lengths, table and q as ``make_inputs``
+    draws them (same seed, same order), the pools' values drawn directly in
+    GPU memory by torch's generator (standard normal float32, the same
+    outlier channels, the same storage casts).  Same shapes, sizes and
+    distributions as ``make_inputs``; different pool values."""
+
+    spec: Spec
+    q: "torch.Tensor"
+    k_pool: "torch.Tensor"
+    v_pool: "torch.Tensor"
+    k_scale: Optional["torch.Tensor"]
+    v_scale: Optional["torch.Tensor"]
+    block_table: "torch.Tensor"
+    context_lens: "torch.Tensor"
+    scale: np.float32
+    ctx_host: np.ndarray
+    num_blocks: int
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.ctx_host.max()) if self.ctx_host.size else 0
+
+    @property
+    def logical_tokens(self) -> int:
+        return int(self.ctx_host.astype(np.int64).sum())
+
+    @property
+    def unique_tokens(self) -> int:
+        s = self.spec
+        shared = (s.shared_prefix_seqs - 1) * s.shared_prefix_tokens if s.shared_prefix_seqs > 1 else 0
+        return self.logical_tokens - shared
+
+
+def _device_pool(gen, n_blocks, hkv, d, kv_dtype, out_ch, gain, device):
+    shape = (n_blocks, BLOCK_SIZE, hkv, d)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[kv_dtype]
+    data = torch.empty(shape, dtype=tdt, device=device)
+    scales = (torch.empty((n_blocks, hkv, BLOCK_SIZE), dtype=torch.float32, device=device)
+              if kv_dtype == "fp8_e4m3" else None)
+    ch = None if out_ch is None or not len(out_ch) else torch.from_numpy(out_ch).to(device)
+    step = max(1, (1 << 26) // (BLOCK_SIZE * hkv * d))
+    for b0 in range(0, n_blocks, step):
+        nb = min(step, n_blocks - b0)
+        x = torch.randn((nb, BLOCK_SIZE, hkv, d), generator=gen, dtype=torch.float32,
+                        device=device)
+        if ch is not None:
+            flat = x.view(nb, BLOCK_SIZE, hkv * d)
+            flat[:, :, ch] *= gain
+        if kv_dtype == "fp8_e4m3":
+            amax = x.abs().amax(dim=-1)
+            sc = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+            y = (x / sc[..., None]).clamp_(-FP8_MAX, FP8_MAX)
+            data[b0:b0 + nb] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+            scales[b0:b0 + nb] = sc.transpose(1, 2)
+        else:
+            data[b0:b0 + nb] = x.to(tdt)
+    return data, scales
+
+
+def make_device_workload(spec: Spec, device="cuda") -> DeviceWorkload:
+    """``spec`` drawn for timing, pools generated on the GPU (seconds instead
+    of the minutes numpy takes for multi-GB pools)."""
+    s = spec
+    rng = np.random.Generator(np.random.PCG64(s.seed))
+    ctx, table, used, n_pool, out_ch, q = _layout_and_queries(s, rng)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(s.seed)
+    k, ks = _device_pool(gen, n_pool, s.num_kv_heads, s.head_dim, s.kv_dtype, out_ch,
+                         s.outlier_gain, device)
+    v, vs = _device_pool(gen, n_pool, s.num_kv_heads, s.head_dim, s.kv_dtype, out_ch,
+                         s.outlier_gain, device)
+    qt = torch.from_numpy(np.ascontiguousarray(q))
+    if q.dtype == np.uint16:
+        qt = qt.view(torch.int16).view(torch.bfloat16)
+    return DeviceWorkload(
+        spec=s, q=qt.to(device), k_pool=k, v_pool=v, k_scale=ks, v_scale=vs,
+        block_table=torch.from_numpy(table).to(device),
+        context_lens=torch.from_numpy(ctx.astype(np.int32)).to(device),
+        scale=np.float32(1.0 / math.sqrt(s.head_dim)), ctx_host=ctx.astype(np.int32),
+        num_blocks=n_pool)
 
 
 def _poison(inp: Inputs) -> None:
