@@ -417,6 +417,29 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
                             size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_run_noalloc -- one decode step that allocates nothing and takes
+ * no workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it).
+ *
+ * Same operation, arguments and results as pa_decode_run (f32 and bf16
+ * pools) and pa_decode_fp8_run (FP8 pools, chosen by the pool's dtype),
+ * minus the workspace: the partial records and arrival counters live in a
+ * file-scope device array of the library, 16 MiB, held on each GPU the
+ * library runs on until the process ends.  The first call on a device looks
+ * up that array's address (hipGetSymbolAddress); every call enqueues, before
+ * the attention kernel, a small kernel that zeroes the counters it will use.
+ * No hipMalloc, hipFree or wait.  All calls on one GPU share the array:
+ * calls that may overlap in time on one GPU (several streams, several host
+ * threads) race and give wrong results; order them.
+ * Limit: launch shapes whose workspace (pa_decode_workspace_bytes) exceeds
+ * 16 MiB are refused with PA_ERR_WORKSPACE (the automatic shape needs at
+ * most 8.8 MiB: 256 workgroups, 32 query heads per workgroup, head_dim 128).
+ * Errors: as pa_decode_run and pa_decode_fp8_run, PA_ERR_WORKSPACE as above.
+ */
+pa_status pa_decode_run_noalloc(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                                int32_t num_q_heads, float scale, float *out, void *stream);
+
+/*
  * pa_decode_set_workgroups -- override the number of workgroups.
  *
  * count: 0 restores the automatic choice (one per compute unit, 256, or

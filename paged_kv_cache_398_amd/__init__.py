@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     pa_decode_heads_per_workgroup,
     pa_decode_kivi_run,
     pa_decode_run,
+    pa_decode_run_noalloc,
     pa_decode_set_heads_per_workgroup,
     pa_decode_set_workgroups,
     pa_decode_workgroups,

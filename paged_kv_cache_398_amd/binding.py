@@ -54,6 +54,7 @@ SIGNATURES = [
     ("pa_decode_workspace_clear", _i32, [_vp, _sz, _vp]),
     ("pa_decode_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     ("pa_decode_fp8_run", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
+    ("pa_decode_run_noalloc", _i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp]),
     ("pa_decode_set_workgroups", _i32, [_vp, _i32]),
     ("pa_decode_workgroups", _i32, [_vp, ctypes.POINTER(_i32)]),
     ("pa_decode_set_heads_per_workgroup", _i32, [_vp, _i32]),
@@ -283,6 +284,11 @@ def pa_decode_fp8_run(pool, q, q_dtype, num_q_heads, scale, out, workspace, work
     _check(load_library().pa_decode_fp8_run(pool, _ptr(q), _dtype(q_dtype), num_q_heads,
                                             float(scale), _ptr(out), _ptr(workspace),
                                             workspace_bytes, _stream(stream)))
+
+
+def pa_decode_run_noalloc(pool, q, q_dtype, num_q_heads, scale, out, stream=None) -> None:
+    _check(load_library().pa_decode_run_noalloc(pool, _ptr(q), _dtype(q_dtype), num_q_heads,
+                                                float(scale), _ptr(out), _stream(stream)))
 
 
 def pa_decode_set_workgroups(pool, count) -> None:

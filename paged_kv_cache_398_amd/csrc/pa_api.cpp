@@ -166,8 +166,13 @@ Layout workspace_layout(const pa_kv_pool *p, int32_t hq) {
   return L;
 }
 
+// Where a run's workspace comes from: the caller's buffer, or the library's
+// static device scratch (pa_decode_run_noalloc).
+enum class Scratch { kCaller, kStatic };
+
 pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, float scale,
-              float *out, void *workspace, size_t ws_bytes, void *stream, bool fp8_entry) {
+              float *out, void *workspace, size_t ws_bytes, void *stream, bool fp8_entry,
+              Scratch from = Scratch::kCaller) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
   if (pool->kivi_bits) return fail(PA_ERR_DTYPE, "an INT8/INT4 pool must be run with pa_decode_kivi_run");
   const bool fp8_pool = pool->kv_dtype == PA_DTYPE_FP8_E4M3;
@@ -190,7 +195,13 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
     return fail(PA_ERR_SHAPE, "scale must be finite");
   if (pool->batch > 0 && (!q || !out)) return fail(PA_ERR_NULL, "q or out is NULL");
   const Layout L = workspace_layout(pool, hq);
-  if (L.total > 0) {
+  if (from == Scratch::kStatic) {
+    if (L.total > pa::kStaticScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "this launch needs %zu bytes of workspace, the static scratch holds %zu "
+                  "(fewer workgroups, or pa_decode_run with a workspace)",
+                  L.total, pa::kStaticScratchBytes);
+  } else if (L.total > 0) {
     if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
     if (ws_bytes < L.total)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
@@ -204,6 +215,17 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   char *ws = static_cast<char *>(workspace);
+  if (from == Scratch::kStatic && L.total > 0) {
+    void *p = nullptr;
+    if ((e = pa::static_scratch(&p)) != hipSuccess)
+      return fail(PA_ERR_HIP, "static scratch: %s", hipGetErrorString(e));
+    // the counters this launch uses must start at zero: runs leave them
+    // zero, but the scratch is shared by every call on this GPU, so clear
+    // them anyway (a kernel, not a memset, so a captured graph replays it)
+    if ((e = pa::launch_zero(static_cast<uint32_t *>(p), (size_t)L.nwg, s)) != hipSuccess)
+      return fail(PA_ERR_HIP, "clearing the static scratch: %s", hipGetErrorString(e));
+    ws = static_cast<char *>(p);
+  }
   pa::LaunchArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
@@ -433,6 +455,13 @@ pa_status pa_decode_fp8_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
                             int32_t num_q_heads, float scale, float *out, void *workspace,
                             size_t workspace_bytes, void *stream) {
   return run(pool, q, q_dtype, num_q_heads, scale, out, workspace, workspace_bytes, stream, true);
+}
+
+pa_status pa_decode_run_noalloc(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
+                                int32_t num_q_heads, float scale, float *out, void *stream) {
+  if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
+  return run(pool, q, q_dtype, num_q_heads, scale, out, nullptr, 0, stream,
+             pool->kv_dtype == PA_DTYPE_FP8_E4M3, Scratch::kStatic);
 }
 
 pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new,

@@ -148,6 +148,13 @@ struct CopyArgs {
 };
 hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
 
+// Bytes of the file-scope device scratch used by pa_decode_run_noalloc.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).  Allocates nothing.
+hipError_t static_scratch(void **ptr);
+
 // Enqueue a kernel that sets n 32-bit words to zero (a kernel rather than a
 // memset, so that a captured graph replays it faithfully).  Only device
 // addresses (a caller's buffer, or a device symbol's address obtained with

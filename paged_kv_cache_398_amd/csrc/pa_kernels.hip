@@ -48,6 +48,9 @@
 
 #include "pa_internal.h"
 
+#include <mutex>
+#include <vector>
+
 namespace pa {
 namespace {
 
@@ -457,20 +460,20 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
 __device__ __forceinline__ float part_weight(float m, float M) { return fast_exp2(m - M); }
 
 // Sum over the workgroup (int64), every thread gets the result.
-__device__ __forceinline__ long long block_sum(long long x, long long *scratch) {
+__device__ __forceinline__ long long block_sum(long long x, long long *part) {
 #pragma unroll
   for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
   __syncthreads();
   long long r = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += scratch[i];
+  for (int i = 0; i < kWaves; ++i) r += part[i];
   return r;
 }
 
 // Inclusive prefix sum over the workgroup (int64); *total gets the sum.
-__device__ __forceinline__ long long block_scan(long long x, long long *scratch, long long *total) {
+__device__ __forceinline__ long long block_scan(long long x, long long *part, long long *total) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off *= 2) {
@@ -478,12 +481,12 @@ __device__ __forceinline__ long long block_scan(long long x, long long *scratch,
     if (lane >= off) x += y;
   }
   __syncthreads();
-  if (lane == 63) scratch[threadIdx.x >> 6] = x;
+  if (lane == 63) part[threadIdx.x >> 6] = x;
   __syncthreads();
   long long before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    const long long v = scratch[i];
+    const long long v = part[i];
     if (i < (int)(threadIdx.x >> 6)) before += v;
     all += v;
   }
@@ -825,6 +828,35 @@ hipError_t launch_attention(const LaunchArgs &a, hipStream_t s) {
     case KV_FP8: return by_dim<KV_FP8>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of pa_decode_run_noalloc, for callers that cannot allocate: a
+// file-scope device array (each GPU the library runs on holds its own copy,
+// at its own address, until the process ends).  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current and kept.
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr) {
+  static std::mutex mu;
+  static std::vector<void *> per_device;  // device address of scratch, by device id
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= per_device.size()) per_device.resize((size_t)dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void *p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_zero(uint32_t *p, size_t n, hipStream_t s) {

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 32
+    assert len(names) == 33
     lib = ctypes.CDLL(pa.binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -168,6 +168,37 @@ def test_workspace_layout_constants():
     assert pa.PA_DECODE_COUNTER_BYTES == 4 * 65536  # one counter per workgroup, at most 65536
     text = open(HEADER).read()
     assert "#define PA_DECODE_COUNTER_BYTES 262144" in text
+
+
+def test_noalloc_refuses_before_any_hip_call():
+    """pa_decode_run_noalloc validates like pa_decode_run and refuses launch
+    shapes whose workspace exceeds its 16 MiB static scratch, all on the
+    host (fake device addresses, no GPU)."""
+    h = pa.pa_kv_pool_create(64, 16, 4, 128, "bf16", K, V)
+    try:
+        run = pa.pa_decode_run_noalloc
+        assert _status(run, h, Q, "bf16", 32, 0.1, OUT, 0) == pa.binding.PA_ERR_STATE
+        pa.pa_block_table_set(h, TBL, CTX, 4, 256, 4096)
+        assert _status(run, h, Q, "f32", 32, 0.1, OUT, 0) == pa.binding.PA_ERR_DTYPE
+        assert _status(run, h, None, "bf16", 32, 0.1, OUT, 0) == pa.binding.PA_ERR_NULL
+        assert _status(run, h, Q, "bf16", 24, 0.1, OUT, 0) == pa.binding.PA_ERR_UNSUPPORTED
+        pa.pa_decode_set_workgroups(h, 4000)
+        assert pa.pa_decode_workspace_bytes(h, 32) > 16 << 20
+        assert _status(run, h, Q, "bf16", 32, 0.1, OUT, 0) == pa.binding.PA_ERR_WORKSPACE
+        assert "static scratch" in pa.pa_last_error()
+        pa.pa_decode_set_workgroups(h, 0)
+        assert pa.pa_decode_workspace_bytes(h, 32) <= 16 << 20
+        pa.pa_block_table_set(h, None, None, 0, 1, 0)
+        run(h, None, "bf16", 32, 0.1, None, 0)  # an empty batch: nothing to do, no HIP call
+    finally:
+        pa.pa_kv_pool_destroy(h)
+    h = pa.pa_kv_pool_create(64, 16, 2, 128, "fp8_e4m3", K, V, KS, VS)
+    try:
+        pa.pa_block_table_set(h, TBL, CTX, 2, 4, 64)
+        assert _status(pa.pa_decode_run_noalloc, h, Q, "f32", 8, 0.1, OUT, 0) == \
+            pa.binding.PA_ERR_DTYPE
+    finally:
+        pa.pa_kv_pool_destroy(h)
 
 
 def test_workspace_clear_errors():
