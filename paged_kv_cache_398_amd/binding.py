@@ -92,6 +92,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with "
                            "`python -m paged_kv_cache_398_amd.build`")
+    # torch's wheel carries its own HIP runtime (same soname as ROCm's).
+    # Loaded first, it is the one libpa.so binds to, so the process has one
+    # runtime; loading libpa.so first would bind torch to the system copy,
+    # and kernel launches then fail with "no ROCm-capable device".
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
     for name, res, args in SIGNATURES:
         fn = getattr(lib, name)

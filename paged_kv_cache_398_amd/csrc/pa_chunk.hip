@@ -61,6 +61,7 @@
 // products, so NaN garbage there cannot leak).
 
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 namespace pa {
 namespace {
@@ -72,11 +73,6 @@ constexpr float kLag = 8.0f;      // lag allowed to the running max (log2 units)
 // running max before any score: finite, so that exp2(x - m) needs no guard;
 // the first visible score always raises it (anything exceeds it by kLag)
 constexpr float kNoMax = -3.402823466e38f;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
 template <int D>
 struct ChunkCfg {
@@ -93,46 +89,6 @@ struct PairRegs {
   int blk;                               // first block of the pair
   bool ok[2];                            // block ids inside the pool
 };
-
-// Maximum over lanes c, c+16, c+32, c+48.  A compare and select: the
-// values are scores or -inf, never NaN, so no quieting of NaN inputs (which
-// fmaxf would add after the lane swaps) is needed.
-__device__ __forceinline__ float max4q(float x) {
-  {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float u = __uint_as_float(r[0]), v = __uint_as_float(r[1]);
-    x = u > v ? u : v;
-  }
-  {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float u = __uint_as_float(r[0]), v = __uint_as_float(r[1]);
-    x = u > v ? u : v;
-  }
-  return x;
-}
-
-__device__ __forceinline__ float max8(const float (&x)[2][4]) {
-  return fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-               fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
-
-// p = hi + lo in bf16: hi is p truncated to bf16 (the upper half of its
-// bits, one byte permute per pair), the remainder p - hi is exact in fp32
-// and below 2^-7 p, and lo is that remainder rounded to the nearest bf16;
-// so hi + lo is within a relative 2^-16 of p.
-__device__ __forceinline__ void split_bf16(const float (&p)[8], bf16x8_t &hi, bf16x8_t &lo) {
-  uint32_t h[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = __float_as_uint(p[2 * i]), b = __float_as_uint(p[2 * i + 1]);
-    h[i] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // upper halves of a (low), b (high)
-    lo[2 * i] = (__bf16)(p[2 * i] - __uint_as_float(a & 0xFFFF0000u));
-    lo[2 * i + 1] = (__bf16)(p[2 * i + 1] - __uint_as_float(b & 0xFFFF0000u));
-  }
-  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
-}
 
 template <int N>
 __device__ __forceinline__ void load_dwords(const char *p, uint32_t *dst) {
@@ -209,7 +165,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   // first position of the tile: a pair ending at or before it is visible to
   // every row of the item, and needs no mask
   const int pfirst = n_ctx - nq + row0 / G;
-  const bf16x8_t ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const bf16x8_t ones = bf16x8_ones();
 
   // ---- lane offsets inside a block (bytes)
   const uint32_t k_off = (uint32_t)(((c * a.hkv + g) * D + 8 * q) * 2);
@@ -525,7 +481,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     for (int m = 0; m < EV; ++m) o[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = a.scale_log2e;
-  const bf16x8_t ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const bf16x8_t ones = bf16x8_ones();
 
   const int *trow = a.table + (size_t)b * a.max_blocks;
   const size_t block_bytes = (size_t)kTok * a.hkv * D * 2;

@@ -47,6 +47,7 @@
 // masked out.
 
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 #include <mutex>
 #include <vector>
@@ -198,10 +199,30 @@ struct Query {
   using C = Cfg<KV, D, G>;
   float f[G][C::EPL];
   uint32_t bf2[G][C::DW];
+  bf16x8_t qm[D / 32];  // MFMA form: lane (row c, quarter q) holds q[h0 + c][32m + 8q .. +7]
 };
+
+// bf16 pools run their products on the matrix cores; f32 and FP8 pools on
+// the vector ALUs.  (The matrix-core form handles FP8 too, widening the
+// codes to bf16 in its LDS tile, but on the FP8 MHA step, one query row per
+// KV head, it measured 402 us against 367 us for the vector form.)
+template <int KV>
+constexpr bool uses_mfma() { return KV == KV_BF16; }
 
 template <int KV, int D, int G>
 __device__ __forceinline__ void load_query(const LaunchArgs &a, int b, int g, Query<KV, D, G> &qry) {
+  if constexpr (uses_mfma<KV>()) {
+    // B operand of S^T = K Q^T: column = query row c (rows G.. are zero),
+    // k = 8 dims at 32m + 8q
+    const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((size_t)b * a.hq + g * G + (c < G ? c : 0)) * D + 8 * q;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+      qry.qm[m] = as_bf16x8(c < G ? *reinterpret_cast<const uint4 *>(qp + 32 * m)
+                                  : make_uint4(0u, 0u, 0u, 0u));
+    return;
+  }
   using C = Cfg<KV, D, G>;
   constexpr int LPT = C::LPT;
   const int lane = threadIdx.x & 63;
@@ -452,6 +473,310 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The matrix-core form of a wave's share of a piece (bf16 and FP8 pools).
+//
+// A wave takes its blocks two at a time (a pair: 32 tokens).  Each load
+// instruction covers whole 128-byte pieces of 8 token rows (16 bytes per
+// lane), the layout that streams fastest: loading straight into the MFMA
+// operand layout (16 rows x 64 bytes per instruction) measured 23% slower
+// as pure loads over the same pools.  The pair is written to a per-wave
+// LDS tile (FP8 codes widened to bf16 on the way, which is exact; slots
+// past the piece's end and blocks outside the pool as zeros) and read back
+// as operands of v_mfma_f32_16x16x32_bf16:
+//  - S^T = K Q^T: A = K (token c of a block, 8 dims at 32m + 8q), B = Q^T
+//    (query row c of the group; rows G..15 zero): lane (c, q) gets row c's
+//    scores of tokens 4q .. 4q+3 of the block.
+//  - O = P V: A = P (the lane's own eight weights: row c, tokens 4q .. 4q+3
+//    of both blocks), B = V from transposing LDS reads (ds_read_b64_tr_b16:
+//    lane (n, q) receives dim 16m + n of those tokens); lane (n, q) then
+//    holds O[rows 4q .. 4q+3][16m + n].  The weights enter as hi + lo bf16
+//    (two products, within a relative 2^-16 of the fp32 weights); the row
+//    sums come from the same two products against a ones operand.  FP8: the
+//    K scale multiplies the score, the V scale the weight of the PV product.
+// The running max is per query row (lanes (c, *)), lagged by kTau; its rare
+// rescale hands the row factors to the output layout through 16 floats of
+// per-wave LDS.
+
+template <int KV, int D>
+struct MCfg {
+  static constexpr int EB = KV == KV_FP8 ? 1 : 2;    // stored bytes per element
+  static constexpr int ROW = D * EB;                 // bytes of one head row in the pool
+  static constexpr int SEG = ROW < 128 ? ROW : 128;  // bytes of a row per load instruction
+  static constexpr int LPR = SEG / 16;               // lanes per row segment (16 B each)
+  static constexpr int RPI = 64 / LPR;               // rows per load instruction
+  static constexpr int NSEG = ROW / SEG;             // segments per row
+  static constexpr int NI = (16 / RPI) * NSEG;       // load instructions per block (K, and V)
+  static constexpr int KM = D / 32;                  // S^T products per block
+  static constexpr int EV = D / 16;                  // 16-dim slabs of O
+  static constexpr int RSK = D * 2 + 16;             // LDS row strides of the bf16 rows (bytes):
+  static constexpr int RSV = D * 2 + 32;             // K and V operand reads cover the banks once
+  static constexpr int TILE = 32 * (RSK + RSV);      // one pair: 32 K rows, then 32 V rows
+  static_assert(16 % RPI == 0 && ROW % SEG == 0, "whole rows per load instruction");
+};
+
+// A pair's loads in flight (registers), and what the compute needs of it.
+template <int KV, int D>
+struct PairLoads {
+  uint4 k[2][MCfg<KV, D>::NI], v[2][MCfg<KV, D>::NI];
+  float4 ks[2], vs[2];  // FP8: scales of tokens 4q .. 4q+3 of each block
+  int tok[2];           // sequence position of each block's slot 0
+  bool ok[2];           // block id inside the pool (no second block: false)
+};
+struct PairMeta {
+  float4 ks[2], vs[2];
+  int tok[2];
+  bool ok[2];
+};
+
+template <int KV, int D, int G>
+__device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, int g, int tok0,
+                                                  int tok_end, int ph, int nph, int w,
+                                                  const Query<KV, D, G> &qry, int tv0,
+                                                  float (*s_acc)[G][D], float (*s_m)[G],
+                                                  float (*s_l)[G], char *tile, float *s_f) {
+  using M = MCfg<KV, D>;
+  constexpr int NI = M::NI, KM = M::KM, EV = M::EV, RSK = M::RSK, RSV = M::RSV;
+  const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+  const int blk0 = tok0 / kBlock;
+  const int nb_w = wave_blocks(tok0, tok_end, ph, nph);
+  const size_t block_bytes = (size_t)kBlock * a.hkv * M::ROW;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+
+  // this lane's row and offsets for load instruction ii: in the pool block
+  // (bytes), and in the bf16 tile row
+  int lrow[NI];
+  uint32_t loff[NI], toff[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    lrow[ii] = (ii / M::NSEG) * M::RPI + lane / M::LPR;
+    const int byte = (ii % M::NSEG) * M::SEG + (lane % M::LPR) * 16;
+    loff[ii] = (uint32_t)((lrow[ii] * a.hkv + g) * M::ROW + byte);
+    toff[ii] = (uint32_t)(byte * (2 / M::EB));
+  }
+
+  // blocks i and i + 1 of the wave (ids id0, id1; -1 past the wave's blocks).
+  // Loads are unconditional (an id outside the pool reads block 0, masked
+  // when staged), so no branch around a load breaks the wait counting.
+  auto issue = [&](PairLoads<KV, D> &P, int i, int id0, int id1) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int id = hb ? id1 : id0;
+      P.tok[hb] = (blk0 + ph + (i + hb) * nph) * kBlock;
+      P.ok[hb] = (unsigned)id < (unsigned)a.num_blocks;
+      const size_t boff = P.ok[hb] ? (size_t)id * block_bytes : 0;
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        if constexpr (KV == KV_FP8) {
+          P.k[hb][ii] = *reinterpret_cast<const uint4 *>(kbase + boff + loff[ii]);
+          P.v[hb][ii] = *reinterpret_cast<const uint4 *>(vbase + boff + loff[ii]);
+        } else {
+          P.k[hb][ii] = load_stream16(kbase + boff + loff[ii]);
+          P.v[hb][ii] = load_stream16(vbase + boff + loff[ii]);
+        }
+      }
+      if constexpr (KV == KV_FP8) {
+        const size_t si = ((P.ok[hb] ? (size_t)id : 0) * a.hkv + g) * kBlock + 4 * q;
+        P.ks[hb] = *reinterpret_cast<const float4 *>(a.k_scale + si);
+        P.vs[hb] = *reinterpret_cast<const float4 *>(a.v_scale + si);
+      }
+    }
+  };
+
+  // write a landed pair into the tile (bf16 rows; dead rows as zeros)
+  auto stage = [&](const PairLoads<KV, D> &P) {
+    PairMeta mt;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const bool all = P.ok[hb] && P.tok[hb] + kBlock <= tok_end;  // wave-uniform
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        const bool live = all || (P.ok[hb] && P.tok[hb] + lrow[ii] < tok_end);
+        const uint32_t mk = live ? 0xFFFFFFFFu : 0u;
+        uint4 kx = P.k[hb][ii], vx = P.v[hb][ii];
+        if (!all) {
+          kx = make_uint4(kx.x & mk, kx.y & mk, kx.z & mk, kx.w & mk);
+          vx = make_uint4(vx.x & mk, vx.y & mk, vx.z & mk, vx.w & mk);
+        }
+        char *kd = tile + (16 * hb + lrow[ii]) * RSK + toff[ii];
+        char *vd = tile + 32 * RSK + (16 * hb + lrow[ii]) * RSV + toff[ii];
+        if constexpr (KV == KV_FP8) {
+          // 16 codes -> 16 bf16 (every E4M3FN value is a bf16 value)
+          auto widen = [](uint4 x, uint4 &lo, uint4 &hi) {
+            const uint32_t d[4] = {x.x, x.y, x.z, x.w};
+            uint32_t r[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              r[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], 1.0f, false));
+              r[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], 1.0f, true));
+            }
+            lo = make_uint4(r[0], r[1], r[2], r[3]);
+            hi = make_uint4(r[4], r[5], r[6], r[7]);
+          };
+          uint4 a0, a1;
+          widen(kx, a0, a1);
+          *reinterpret_cast<uint4 *>(kd) = a0;
+          *reinterpret_cast<uint4 *>(kd + 16) = a1;
+          widen(vx, a0, a1);
+          *reinterpret_cast<uint4 *>(vd) = a0;
+          *reinterpret_cast<uint4 *>(vd + 16) = a1;
+        } else {
+          *reinterpret_cast<uint4 *>(kd) = kx;
+          *reinterpret_cast<uint4 *>(vd) = vx;
+        }
+      }
+      mt.tok[hb] = P.tok[hb];
+      mt.ok[hb] = P.ok[hb];
+      mt.ks[hb] = P.ks[hb];
+      mt.vs[hb] = P.vs[hb];
+    }
+    return mt;
+  };
+
+  float mrun = kNoMax;  // running max of query row c
+  f32x4_t o[EV], l4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < EV; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones = bf16x8_ones();
+  const float sl2 = a.scale_log2e;
+
+  auto compute = [&](const PairMeta &mt) {
+    __builtin_amdgcn_wave_barrier();  // the tile's rows were written by other lanes
+    f32x4_t sc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const uint4 kop = *reinterpret_cast<const uint4 *>(tile + (16 * hb + c) * RSK + (32 * m + 8 * q) * 2);
+        sc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), qry.qm[m], sc[hb], 0, 0, 0);
+      }
+    }
+    const bool full = mt.ok[0] && mt.ok[1] && mt.tok[0] + kBlock <= tok_end &&
+                      mt.tok[1] + kBlock <= tok_end;  // wave-uniform
+    float x[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float kscale[4] = {mt.ks[hb].x, mt.ks[hb].y, mt.ks[hb].z, mt.ks[hb].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[hb][j] = sc[hb][j] * sl2;
+        if constexpr (KV == KV_FP8) x[hb][j] *= kscale[j];
+      }
+    }
+    if (!full) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[hb][j] = (mt.ok[hb] && mt.tok[hb] + 4 * q + j < tok_end) ? x[hb][j] : -__builtin_huge_valf();
+    }
+    const float mx = max4q(max8(x));
+    const bool raise = mx > mrun + kTau;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float mn = raise ? mx : mrun;
+      const float f = raise ? fast_exp2(mrun - mn) : 1.f;
+      mrun = mn;
+      // lane (c, q) has row c's factor; its O and l entries are rows 4q .. 4q+3
+      if (q == 0) s_f[c] = f;
+      __builtin_amdgcn_wave_barrier();
+      const float4 f4 = *reinterpret_cast<const float4 *>(&s_f[4 * q]);
+      __builtin_amdgcn_wave_barrier();
+      const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        l4[r] *= fr[r];
+#pragma unroll
+        for (int m = 0; m < EV; ++m) o[m][r] *= fr[r];
+      }
+    }
+    float pf[8];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pf[4 * hb + j] = fast_exp2(x[hb][j] - mrun);  // masked: 0
+    bf16x8_t ph, pl;
+    split_bf16(pf, ph, pl);
+    l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4, 0, 0, 0);
+    l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4, 0, 0, 0);
+    bf16x8_t wh = ph, wl = pl;
+    if constexpr (KV == KV_FP8) {
+      float pv[8];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float vscale[4] = {mt.vs[hb].x, mt.vs[hb].y, mt.vs[hb].z, mt.vs[hb].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float t = pf[4 * hb + j] * vscale[j];
+          // a dead slot's scale may be anything (NaN included): its weight is 0
+          pv[4 * hb + j] = full || (mt.ok[hb] && mt.tok[hb] + 4 * q + j < tok_end) ? t : 0.f;
+        }
+      }
+      split_bf16(pv, wh, wl);
+    }
+    const char *lv = tile + 32 * RSK;
+#pragma unroll
+    for (int m = 0; m < EV; ++m) {
+      v4s_t h[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
+      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vb, o[m], 0, 0, 0);
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vb, o[m], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: pairs p, two stages: pair p is staged and computed while
+  // pairs p + 1 and p + 2 are in flight.  The table entries of up to 64
+  // blocks come from one vector load (lane j holds block c0 + j; -1 past
+  // the wave's blocks), read with readlane.
+  for (int c0 = 0; c0 < nb_w; c0 += 64) {
+    const int cn = min(64, nb_w - c0);
+    const int tv = c0 == 0 ? tv0 : load_table(a, b, blk0, ph, nph, c0, nb_w);
+    auto entry = [&](int i) { return __builtin_amdgcn_readlane(tv, i); };  // i < 64
+    const int np = (cn + 1) / 2;
+    PairLoads<KV, D> A, B;
+    issue(A, c0, entry(0), entry(1));
+    if (np > 1) issue(B, c0 + 2, entry(2), entry(3));
+    int p = 0;
+    for (; p + 3 < np; p += 2) {
+      const PairMeta ma = stage(A);
+      issue(A, c0 + 2 * p + 4, entry(2 * p + 4), entry(2 * p + 5));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ma);
+      const PairMeta mb = stage(B);
+      issue(B, c0 + 2 * p + 6, entry(2 * p + 6), entry(2 * p + 7));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(mb);
+    }
+    // at most three pairs left: p (in A), p + 1 (in B), p + 2 (not issued)
+    if (p < np) {
+      const PairMeta ma = stage(A);
+      if (p + 2 < np) issue(A, c0 + 2 * p + 4, entry(2 * p + 4), entry(2 * p + 5));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ma);
+    }
+    if (p + 1 < np) compute(stage(B));
+    if (p + 2 < np) compute(stage(A));
+  }
+
+  // ---- the wave's state by query row hh < G: the max in lanes (hh, *);
+  // sums and output rows 4q .. 4q+3 in lanes (n, q)
+  if (q == 0 && c < G) s_m[w][c] = mrun;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hh = 4 * q + r;
+    if (hh < G) {
+      if (c == 0) s_l[w][hh] = l4[r];
+#pragma unroll
+      for (int m = 0; m < EV; ++m) s_acc[w][hh][16 * m + c] = o[m][r];
+    }
+  }
+}
+
 // Exact combination of weighted partial states: the running maxima of the
 // parts are aligned to their common maximum M.  A part that saw no valid
 // token has m = kNoMax and l = acc = 0: its weight is 0 next to any part
@@ -519,6 +844,9 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   __shared__ long long s_first[3];  // first sequence, its first unit, its length
   __shared__ int s_len[kThreads];     // clamped lengths, when batch <= kThreads
   __shared__ int s_last;
+  // per-wave staging tiles and rescale factors of the matrix-core form
+  __shared__ __align__(16) char s_tile[uses_mfma<KV>() ? kWaves * MCfg<KV, D>::TILE : 16];
+  __shared__ __align__(16) float s_fw[kWaves][16];
 
   const int tid = threadIdx.x;
   // wave index, known wave-uniform: everything derived from it stays scalar
@@ -666,13 +994,19 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     // the guess holds when every sequence has max_ctx tokens' worth of
     // blocks and this one exactly max_ctx tokens: then the first piece is
     // the guessed one, same blocks and same tail
+    auto piece = [&](const Query<KV, D, G> &qr, int tvr) {
+      if constexpr (uses_mfma<KV>())
+        attend_piece_mfma<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qr, tvr, s_acc, s_m, s_l,
+                                    s_tile + (uses_mfma<KV>() ? w * MCfg<KV, D>::TILE : 0), s_fw[w]);
+      else
+        attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qr, tvr, s_acc, s_m, s_l);
+    };
     if (first_piece && full && U == Ug && n == a.max_ctx) {
-      attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qry_g, tv_g, s_acc, s_m, s_l);
+      piece(qry_g, tv_g);
     } else {
       Query<KV, D, G> qry;
       load_query<KV, D, G>(a, b, g, qry);
-      const int tv = load_table(a, b, blk_lo, ph, nph, 0, wave_blocks(tok0, tok_end, ph, nph));
-      attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qry, tv, s_acc, s_m, s_l);
+      piece(qry, load_table(a, b, blk_lo, ph, nph, 0, wave_blocks(tok0, tok_end, ph, nph)));
     }
     __syncthreads();
 
