@@ -221,13 +221,15 @@ pa_status pa_cache_append(pa_kv_pool *pool, const void *k_new, const void *v_new
  *   output rows are not written).
  * max_q_len: host bound of n_b; it sizes the grid.
  * out: device float32 [total_q][num_q_heads][head_dim].
- * Only bf16 pools (and bf16 q); head_dim 64 or 128; num_q_heads / num_kv_heads
- * in {1, 2, 4, 8}.  Both products run in bf16 on the matrix cores with fp32
- * accumulation; the softmax weights enter the PV product rounded to bf16
- * (each within a relative 2^-9; the normaliser sums the same rounded
- * weights).  No workspace; asynchronous on `stream`.
+ * bf16 and FP8 E4M3 pools (q bf16); head_dim 64 or 128; num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8}.  Both products run in bf16 on the matrix
+ * cores with fp32 accumulation: FP8 codes are widened to bf16 exactly, the
+ * K scale multiplies the fp32 score and the V scale the softmax weight (the
+ * d7kj.com page, section 四); each weight enters the PV product as the sum
+ * of two bf16 values, within a relative 2^-16 of its fp32 value, and the
+ * normaliser sums the same values.  No workspace; asynchronous on `stream`.
  * Errors: PA_ERR_NULL, PA_ERR_STATE (no table set), PA_ERR_DTYPE,
- *   PA_ERR_UNSUPPORTED (pool not bf16, group size), PA_ERR_SHAPE,
+ *   PA_ERR_UNSUPPORTED (f32 or INT8/INT4 pool, group size), PA_ERR_SHAPE,
  *   PA_ERR_HIP.
  */
 pa_status pa_chunk_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t num_q_heads,

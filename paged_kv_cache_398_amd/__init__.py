@@ -174,11 +174,11 @@ class PagedKVPool:
         pa_cache_append(self.handle, k_new, v_new, src, stream)
 
     def chunk(self, q, q_start, max_q_len, out, scale=None, stream=None):
-        """Attention of several new tokens per sequence: ``q`` [T][Hq][d]
-        bf16 (rows of sequence b are q_start[b] .. q_start[b+1]-1, the last
-        of its cached positions), ``q_start`` device int32 [B+1],
-        ``max_q_len`` host bound of the rows per sequence -> ``out`` float32
-        [T][Hq][d]."""
+        """Attention of several new tokens per sequence (bf16 or FP8 pool):
+        ``q`` [T][Hq][d] bf16 (rows of sequence b are q_start[b] ..
+        q_start[b+1]-1, the last of its cached positions), ``q_start`` device
+        int32 [B+1], ``max_q_len`` host bound of the rows per sequence ->
+        ``out`` float32 [T'][Hq][d], T' >= T."""
         self._need_table()
         if len(q.shape) != 3:
             raise ValueError(f"q has shape {tuple(q.shape)}, expected [T][Hq][{self.head_dim}]")

@@ -642,14 +642,14 @@ pa_status pa_chunk_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_
                        float *out, void *stream) {
   if (!pool) return fail(PA_ERR_NULL, "pool is NULL");
   if (!pool->table_set) return fail(PA_ERR_STATE, "no block table set (pa_block_table_set)");
-  if (pool->kv_dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "chunk attention is built for bf16 pools only");
+  if (pool->kivi_bits || (pool->kv_dtype != PA_DTYPE_BF16 && pool->kv_dtype != PA_DTYPE_FP8_E4M3))
+    return fail(PA_ERR_UNSUPPORTED, "chunk attention is built for bf16 and FP8 pools");
   if (q_dtype != PA_DTYPE_BF16) return fail(PA_ERR_DTYPE, "chunk attention needs bf16 q");
   if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads)
     return fail(PA_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 num_q_heads, pool->num_kv_heads);
   const int group = num_q_heads / pool->num_kv_heads;
-  if (!pa::chunk_supported(pool->head_dim, group))
+  if (!pa::chunk_supported(kind_of(pool->kv_dtype), pool->head_dim, group))
     return fail(PA_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", group);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale must be finite");
   if (total_q < 0 || max_q_len < 0)
@@ -665,6 +665,9 @@ pa_status pa_chunk_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_
   pa::ChunkArgs a{};
   a.k_cache = pool->k_cache;
   a.v_cache = pool->v_cache;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.kv = kind_of(pool->kv_dtype);
   a.q = q;
   a.table = pool->block_table;
   a.ctx = pool->context_lens;

@@ -81,39 +81,21 @@ struct ChunkCfg {
   static constexpr int VDW = EV / 2;  // dwords of that slice
 };
 
-// One lane's share of a pair of blocks.
-template <int D>
-struct PairRegs {
-  uint4 k[2][ChunkCfg<D>::KM];           // token lane%16, dims 32m + 8(lane/16) .. +7
-  uint32_t v[2][4][ChunkCfg<D>::VDW];    // tokens 4(lane/16)+j, dims EV*(lane%16) ..
-  int blk;                               // first block of the pair
-  bool ok[2];                            // block ids inside the pool
-};
-
-template <int N>
-__device__ __forceinline__ void load_dwords(const char *p, uint32_t *dst) {
-  if constexpr (N == 4) {
-    const uint4 x = load_stream16(p);
-    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
-  } else {
-    static_assert(N == 2, "8- or 16-byte slices");
-    const uint2 x = load_stream8(p);
-    dst[0] = x.x; dst[1] = x.y;
-  }
-}
-
-template <int D, int G, int NQT>
+template <int KV, int D, int G, int NQT>
 __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
-  using C = ChunkCfg<D>;
-  constexpr int KM = C::KM, EV = C::EV, VDW = C::VDW;
+  using M = MCfg<KV, D>;
+  constexpr int KM = M::KM, EV = M::EV, RSK = M::RSK;
   constexpr int ROWS = 16 * NQT;
-  constexpr int OS = D + 4;  // LDS row stride (floats), spreads the banks
+  constexpr int OS = D + 4;  // LDS row stride (floats) of the combine, spreads the banks
+  __shared__ __align__(16) char s_tile[kCW * M::TILE];
   __shared__ float s_o[kCW][16][OS];
   __shared__ float s_m[kCW][ROWS], s_l[kCW][ROWS];
+  __shared__ __align__(16) float s_f[kCW][16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, q = lane >> 4;
+  char *tile = s_tile + w * M::TILE;
 
   // ---- the item: consecutive workgroup indices alternate between the 8
   // XCDs, so each XCD is given a contiguous run of items (the tiles of one
@@ -123,7 +105,7 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   const int xcd = (int)(blockIdx.x % 8);
   const long long item = xcd * per + min((long long)xcd, rem) + blockIdx.x / 8;
   const int bg = (int)(item / a.tiles);
-  const int tile = a.tiles - 1 - (int)(item % a.tiles);
+  const int tile_i = a.tiles - 1 - (int)(item % a.tiles);
   const int b = bg / a.hkv, g = bg % a.hkv;
 
   const int n_ctx = min(max(a.ctx[b], 0), a.max_ctx);
@@ -131,18 +113,20 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   // no rows, or offsets that would leave q/out: nothing to do
   if (nq <= 0 || nq > a.max_q || r0 < 0 || r0 > a.total_q - nq) return;
   const int nrows = nq * G;
-  const int row0 = tile * ROWS;
+  const int row0 = tile_i * ROWS;
   if (row0 >= nrows) return;
   const int last_row = min(row0 + ROWS, nrows) - 1;
-  const int pmax = n_ctx - nq + last_row / G;  // position of the tile's last row
+  const int pmax = n_ctx - nq + last_row / G;  // position of the item's last row
   const int nblk = pmax >= 0 ? pmax / kTok + 1 : 0;
   const int npairs = (nblk + 1) / 2;
 
-  // ---- query rows of the tile (B operands of S^T), positions, state
+  // ---- query rows of each 16-row tile (B operands of S^T: column = row c),
+  // their positions, and the online-softmax state: max per row in lanes
+  // (c, *); sums and output rows 4q .. 4q+3 in lanes (n, q)
   bf16x8_t qf[NQT][KM];
   int prow[NQT];
   f32x4_t o[NQT][EV];
-  f32x4_t l4[NQT];  // row sums of the rounded weights, all four entries equal
+  f32x4_t l4[NQT];
   float mrun[NQT];
   const float sl2 = a.scale_log2e;
 #pragma unroll
@@ -162,140 +146,118 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
     for (int m = 0; m < EV; ++m) o[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // first position of the tile: a pair ending at or before it is visible to
-  // every row of the item, and needs no mask
+  // first position of the item: a pair ending at or before it is visible to
+  // every row, and needs no mask
   const int pfirst = n_ctx - nq + row0 / G;
   const bf16x8_t ones = bf16x8_ones();
 
-  // ---- lane offsets inside a block (bytes)
-  const uint32_t k_off = (uint32_t)(((c * a.hkv + g) * D + 8 * q) * 2);
-  const uint32_t v_off = (uint32_t)((((4 * q) * a.hkv + g) * D + EV * c) * 2);
-  const uint32_t v_step = (uint32_t)(a.hkv * D * 2);  // one token row
-  const size_t block_bytes = (size_t)kTok * a.hkv * D * 2;
-  const char *kbase = static_cast<const char *>(a.k_cache);
-  const char *vbase = static_cast<const char *>(a.v_cache);
+  const StageLanes<KV, D> sl = stage_lanes<KV, D>(a.hkv, g);
+  const size_t block_bytes = (size_t)kTok * a.hkv * M::ROW;
+  auto issue = [&](PairLoads<KV, D> &P, int pair, int id0, int id1) {
+    issue_pair<KV, D>(P, sl, a.k_cache, a.v_cache, a.k_scale, a.v_scale, block_bytes, a.hkv, g,
+                      a.num_blocks, id0, id1, 2 * pair * kTok, (2 * pair + 1) * kTok);
+  };
 
-  // loads of a pair are issued unconditionally: an id outside the pool
-  // reads block 0 and is masked in compute
-  auto issue = [&](PairRegs<D> &P, int pair, int id0, int id1) {
-    P.blk = 2 * pair;
+  auto compute = [&](const PairMeta &mt) {
+    __builtin_amdgcn_wave_barrier();  // the tile's rows were written by other lanes
+    // K operands (A of S^T: token c of block hb, dims 32m + 8q) and V
+    // operands (B of O = P V), shared by the NQT row tiles
+    uint4 kop[2][KM];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int id = hb ? id1 : id0;
-      P.ok[hb] = (unsigned)id < (unsigned)a.num_blocks;
-      const size_t boff = P.ok[hb] ? (size_t)id * block_bytes : 0;
-      const char *kb = kbase + boff, *vb = vbase + boff;
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int m = 0; m < KM; ++m)
-        P.k[hb][m] = load_stream16(kb + (k_off + 64 * m));
+        kop[hb][m] = *reinterpret_cast<const uint4 *>(tile + (16 * hb + c) * RSK + (32 * m + 8 * q) * 2);
+    bf16x8_t vb[EV];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_dwords<VDW>(vb + (v_off + j * v_step), P.v[hb][j]);
-    }
-  };
-
-  // A operand of O^T product m: element m of the lane's 8 V rows
-  auto v_operand = [&](const PairRegs<D> &P, int m) {
-    uint32_t d4[4];
+    for (int m = 0; m < EV; ++m) vb[m] = v_operand_tr<D>(tile + 32 * RSK, M::RSV, m);
+    // the whole pair visible to every row, both blocks in the pool: no mask
+    const bool full = mt.ok[0] && mt.ok[1] && mt.tok[1] + kTok - 1 <= pfirst;
 #pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int hb = k2 >> 1, j0 = (k2 & 1) * 2;
-      // low half from token j0's dword, high half from token j0 + 1's: the
-      // even or odd element of the pair of dims the dwords hold
-      d4[k2] = __builtin_amdgcn_perm(P.v[hb][j0 + 1][m >> 1], P.v[hb][j0][m >> 1],
-                                     (m & 1) ? 0x07060302u : 0x05040100u);
-    }
-    return as_bf16x8(make_uint4(d4[0], d4[1], d4[2], d4[3]));
-  };
-
-  // full: both blocks inside the pool and every token of the pair at or
-  // before the first row's position -- no mask, no zeroed V rows (a
-  // wave-uniform branch; only a row tile's last pairs are not full).
-  auto compute = [&](PairRegs<D> &P) {
-    const bool full = P.ok[0] && P.ok[1] && (P.blk + 2) * kTok - 1 <= pfirst;
-    if (!full) {
-      // V rows of slots past the cached tokens (or of a block id outside
-      // the pool) may hold anything, NaN included: zero them by select,
-      // since a zero weight times NaN would still be NaN in the product
-      if (!P.ok[0] || !P.ok[1] || (P.blk + 2) * kTok > n_ctx) {
+    for (int t = 0; t < NQT; ++t) {
+      f32x4_t sc[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        sc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < KM; ++m)
+          sc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[t][m], sc[hb], 0, 0, 0);
+      }
+      // scaled scores (log2 units) of row c, tokens 4q .. 4q+3 of each block
+      float x[2][4];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float ksc[4] = {mt.ks[hb].x, mt.ks[hb].y, mt.ks[hb].z, mt.ks[hb].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[hb][j] = sc[hb][j] * sl2;
+          if constexpr (KV == KV_FP8) x[hb][j] *= ksc[j];
+        }
+      }
+      if (!full) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bool real = P.ok[hb] && (P.blk + hb) * kTok + 4 * q + j < n_ctx;
-#pragma unroll
-            for (int k = 0; k < VDW; ++k) P.v[hb][j][k] = real ? P.v[hb][j][k] : 0u;
-          }
-      }
-    }
-    // the A operands of O^T (V^T, one per product m) depend on the pair
-    // only: built once for the NQT tiles
-    bf16x8_t va[EV];
-#pragma unroll
-    for (int m = 0; m < EV; ++m) va[m] = v_operand(P, m);
-#pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      f32x4_t s[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        s[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < KM; ++m)
-          s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(P.k[hb][m]), qf[t][m], s[hb], 0, 0, 0);
-      }
-      // scaled scores in log2 units.  Their maximum is taken in the block
-      // that forms the products, so its operands are known canonical floats
-      // (no NaN quieting before v_max3); a pair with masked slots takes it
-      // again over the masked values.
-      float x[2][4];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[hb][j] = s[hb][j] * sl2;
-      float mx = max8(x);
-      if (!full) {
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int tok0 = (P.blk + hb) * kTok + 4 * q;
-#pragma unroll
           for (int j = 0; j < 4; ++j)
-            x[hb][j] = (P.ok[hb] && tok0 + j <= prow[t]) ? x[hb][j] : -__builtin_huge_valf();
-        }
-        mx = max8(x);
+            x[hb][j] = (mt.ok[hb] && mt.tok[hb] + 4 * q + j <= prow[t]) ? x[hb][j] : -__builtin_huge_valf();
       }
-      mx = max4q(mx);
+      const float mx = max4q(max8(x));
       const bool raise = mx > mrun[t] + kLag;
       if (__builtin_amdgcn_ballot_w64(raise)) {
         const float mn = raise ? mx : mrun[t];
         const float f = raise ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
         mrun[t] = mn;
-        l4[t] *= f;
+        // lane (c, q) has row c's factor; its O and l entries are rows 4q .. 4q+3
+        if (q == 0) s_f[w][c] = f;
+        __builtin_amdgcn_wave_barrier();
+        const float4 f4 = *reinterpret_cast<const float4 *>(&s_f[w][4 * q]);
+        __builtin_amdgcn_wave_barrier();
+        const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-        for (int m = 0; m < EV; ++m) o[t][m] *= f;
+        for (int r = 0; r < 4; ++r) {
+          l4[t][r] *= fr[r];
+#pragma unroll
+          for (int m = 0; m < EV; ++m) o[t][m][r] *= fr[r];
+        }
       }
       const float nm = -mrun[t];
       float pf[8];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // a masked score (-inf) gives exactly 0
-          pf[4 * hb + j] = __builtin_amdgcn_exp2f(x[hb][j] + nm);
-        }
+        for (int j = 0; j < 4; ++j) pf[4 * hb + j] = __builtin_amdgcn_exp2f(x[hb][j] + nm);  // masked: 0
       bf16x8_t ph, pl;
       split_bf16(pf, ph, pl);
       // the normaliser sums the same weights (hi + lo), on the matrix cores
-      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph, l4[t], 0, 0, 0);
-      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl, l4[t], 0, 0, 0);
+      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4[t], 0, 0, 0);
+      l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4[t], 0, 0, 0);
+      bf16x8_t wh = ph, wl = pl;
+      if constexpr (KV == KV_FP8) {  // the V scale multiplies the PV weight
+        float pv[8];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const float vsc[4] = {mt.vs[hb].x, mt.vs[hb].y, mt.vs[hb].z, mt.vs[hb].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = pf[4 * hb + j] * vsc[j];
+            // a masked slot's scale may be anything (NaN included): weight 0
+            pv[4 * hb + j] = (full || (mt.ok[hb] && mt.tok[hb] + 4 * q + j <= prow[t])) ? v : 0.f;
+          }
+        }
+        split_bf16(pv, wh, wl);
+      }
 #pragma unroll
       for (int m = 0; m < EV; ++m) {
-        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], ph, o[t][m], 0, 0, 0);
-        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pl, o[t][m], 0, 0, 0);
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vb[m], o[t][m], 0, 0, 0);
+        o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vb[m], o[t][m], 0, 0, 0);
       }
     }
   };
-  // ---- main loop: the wave's pairs w, w+4, ..., in chunks of 32 pairs
-  // whose 64 table entries are read by one vector load; a two-stage
-  // pipeline keeps the next pair's loads in flight while one is computed.
+
+  // ---- main loop: the wave's pairs w, w+4, ..., in chunks of 32 pairs whose
+  // 64 table entries are read by one vector load (-1 past the visible
+  // blocks); pair i is staged and computed while pairs i+1 and i+2 are in
+  // flight.
   const int npw = npairs > w ? (npairs - w + kCW - 1) / kCW : 0;
   const int *trow = a.table + (size_t)b * a.max_blocks;
   for (int i0 = 0; i0 < npw; i0 += 32) {
@@ -305,48 +267,53 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
       const int blk = 2 * (w + kCW * (i0 + (lane >> 1))) + (lane & 1);
       tv = blk < nblk ? trow[blk] : -1;
     }
-    auto id_of = [&](int i, int hb) { return __builtin_amdgcn_readlane(tv, 2 * i + hb); };
+    auto id_of = [&](int i, int hb) { return __builtin_amdgcn_readlane(tv, 2 * i + hb); };  // i < 32
     auto pair_of = [&](int i) { return w + kCW * (i0 + i); };
-    PairRegs<D> A, B;
+    PairLoads<KV, D> A, B;
     issue(A, pair_of(0), id_of(0, 0), id_of(0, 1));
+    if (cn > 1) issue(B, pair_of(1), id_of(1, 0), id_of(1, 1));
     int i = 0;
-    for (; i + 2 < cn; i += 2) {
-      issue(B, pair_of(i + 1), id_of(i + 1, 0), id_of(i + 1, 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(A);
+    for (; i + 3 < cn; i += 2) {
+      const PairMeta ma = stage_pair<KV, D>(A, sl, tile, n_ctx);
       issue(A, pair_of(i + 2), id_of(i + 2, 0), id_of(i + 2, 1));
       __builtin_amdgcn_sched_barrier(0);
-      compute(B);
-    }
-    if (i + 1 < cn) {
-      issue(B, pair_of(i + 1), id_of(i + 1, 0), id_of(i + 1, 1));
+      compute(ma);
+      const PairMeta mb = stage_pair<KV, D>(B, sl, tile, n_ctx);
+      issue(B, pair_of(i + 3), id_of(i + 3, 0), id_of(i + 3, 1));
       __builtin_amdgcn_sched_barrier(0);
-      compute(A);
-      compute(B);
-    } else {
-      compute(A);
+      compute(mb);
     }
+    // at most three pairs left: i (in A), i + 1 (in B), i + 2 (not issued)
+    if (i < cn) {
+      const PairMeta ma = stage_pair<KV, D>(A, sl, tile, n_ctx);
+      if (i + 2 < cn) issue(A, pair_of(i + 2), id_of(i + 2, 0), id_of(i + 2, 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ma);
+    }
+    if (i + 1 < cn) compute(stage_pair<KV, D>(B, sl, tile, n_ctx));
+    if (i + 2 < cn) compute(stage_pair<KV, D>(A, sl, tile, n_ctx));
   }
 
   // ---- combine the four waves exactly, one 16-row tile at a time
 #pragma unroll
   for (int t = 0; t < NQT; ++t) {
-    if (q == 0) {
-      s_m[w][16 * t + c] = mrun[t];
-      s_l[w][16 * t + c] = l4[t][0];
+    if (q == 0) s_m[w][16 * t + c] = mrun[t];
+    if (c == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_l[w][16 * t + 4 * q + r] = l4[t][r];
     }
-  }
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int t = 0; t < NQT; ++t) {
-    float M = kNoMax;
+    for (int r = 0; r < 4; ++r) {  // rows 4q + r of the tile: weight exp2(m_w - M)
+      const int rr = 16 * t + 4 * q + r;
+      float M = kNoMax;
 #pragma unroll
-    for (int v = 0; v < kCW; ++v) M = fmaxf(M, s_m[v][16 * t + c]);
-    const float f = mrun[t] == kNoMax ? 0.f : __builtin_amdgcn_exp2f(mrun[t] - M);
+      for (int v = 0; v < kCW; ++v) M = fmaxf(M, s_m[v][rr]);
+      const float mw = s_m[w][rr];
+      const float f = mw == kNoMax ? 0.f : __builtin_amdgcn_exp2f(mw - M);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int m = 0; m < EV; ++m) s_o[w][c][4 * EV * q + EV * j + m] = o[t][m][j] * f;
+      for (int m = 0; m < EV; ++m) s_o[w][4 * q + r][16 * m + c] = o[t][m][r] * f;
+    }
     __syncthreads();
     for (int idx = tid; idx < 16 * (D / 4); idx += kCThreads) {
       const int cc = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
@@ -397,7 +364,7 @@ constexpr int kSR = kSB * 16;             // token rows per stage
 template <int D>
 constexpr int phase_tiles() { return D == 64 ? kWT : 1; }
 
-template <int D>
+template <int KV, int D>
 struct WideCfg {
   // LDS row strides (bytes), one per region, each making its reads
   // conflict-free: a K operand read takes 16 B of one row per lane, lanes
@@ -409,16 +376,18 @@ struct WideCfg {
   // active cycles in the counters.)
   static constexpr int RSK = D * 2 + 16;
   static constexpr int RSV = D * 2 + 32;
-  static constexpr int ROWCH = D / 8;                  // 16-byte chunks per token row
+  static constexpr int EB = KV == KV_FP8 ? 1 : 2;      // stored bytes per element
+  static constexpr int ROWB = D * EB;                  // bytes of a token row (one head) in the pool
+  static constexpr int ROWCH = ROWB / 16;              // 16-byte chunks per token row
   static constexpr int NCH = (kSR * ROWCH + kWThreads - 1) / kWThreads;  // chunks per thread per stage (K, and V)
   static constexpr bool ALL = kSR * ROWCH % kWThreads == 0;             // every thread has NCH chunks
   static constexpr int STAGE = kSR * (RSK + RSV);      // one stage: kSR K rows, then kSR V rows
 };
 
-template <int D, int G>
+template <int KV, int D, int G>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW / 4))) void chunk_wide_kernel(ChunkArgs a) {
   using C = ChunkCfg<D>;
-  using WC = WideCfg<D>;
+  using WC = WideCfg<KV, D>;
   constexpr int KM = C::KM, EV = C::EV;
   constexpr int RSK = WC::RSK, RSV = WC::RSV, NCH = WC::NCH, ROWCH = WC::ROWCH;
   constexpr int kPH = phase_tiles<D>();
@@ -426,6 +395,8 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   constexpr bool ALL = WC::ALL;
   __shared__ __align__(16) char s_kv[2 * WC::STAGE];
   __shared__ __align__(16) float s_f[kWW][16];  // per-row rescaling factors
+  // FP8: the K and V scales of each stage's tokens (0 for slots not real)
+  __shared__ __align__(16) float s_sc[KV == KV_FP8 ? 2 : 1][2][kSR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -484,7 +455,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   const bf16x8_t ones = bf16x8_ones();
 
   const int *trow = a.table + (size_t)b * a.max_blocks;
-  const size_t block_bytes = (size_t)kTok * a.hkv * D * 2;
+  const size_t block_bytes = (size_t)kTok * a.hkv * WC::ROWB;
   const char *kbase = static_cast<const char *>(a.k_cache);
   const char *vbase = static_cast<const char *>(a.v_cache);
   auto block_id = [&](int blk) { return blk < nblk ? trow[blk] : -1; };
@@ -497,6 +468,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   uint4 sk[NCH], sv[NCH];
   bool sreal[NCH];
   bool sall = true;  // every slot of the stage real (wave-uniform)
+  float ssc = 0.f;   // FP8: the scale thread tid < 2 kSR moves (K for tid < kSR, then V)
   auto stage_load = [&](int sg) {
     const int blk0 = kSB * sg;
     int id[kSB];
@@ -517,21 +489,49 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       for (int h = 1; h < kSB; ++h) bid = hb == h ? id[h] : bid;
       const bool ok = (unsigned)bid < (unsigned)a.num_blocks;
       sreal[i] = ok && (blk0 + hb) * kTok + slot < n_ctx;
-      const size_t off = (ok ? (size_t)bid * block_bytes : 0) + (size_t)(((slot * a.hkv + g) * D + col * 8) * 2);
+      const size_t off = (ok ? (size_t)bid * block_bytes : 0) + (size_t)((slot * a.hkv + g) * WC::ROWB + col * 16);
       sk[i] = *reinterpret_cast<const uint4 *>(kbase + off);
       sv[i] = *reinterpret_cast<const uint4 *>(vbase + off);
     }
+    if constexpr (KV == KV_FP8) {
+      if (tid < 2 * kSR) {
+        const int r = tid % kSR, hb = r >> 4, slot = r & 15;
+        int bid = id[0];
+#pragma unroll
+        for (int h = 1; h < kSB; ++h) bid = hb == h ? id[h] : bid;
+        const bool ok = (unsigned)bid < (unsigned)a.num_blocks;
+        const float *sc = tid < kSR ? a.k_scale : a.v_scale;
+        const float x = sc[((ok ? (size_t)bid : 0) * a.hkv + g) * kTok + slot];
+        ssc = ok && (blk0 + hb) * kTok + slot < n_ctx ? x : 0.f;
+      }
+    }
   };
+  // one 16-byte chunk of a K or V row into the stage: bf16 as it is, FP8
+  // codes widened to 32 bytes of bf16
+  auto put = [&](char *dst, uint4 x) {
+    if constexpr (KV == KV_FP8) {
+      uint4 lo, hi;
+      widen_fp8x16(x, lo, hi);
+      reinterpret_cast<uint4 *>(dst)[0] = lo;
+      reinterpret_cast<uint4 *>(dst)[1] = hi;
+    } else {
+      *reinterpret_cast<uint4 *>(dst) = x;
+    }
+  };
+  constexpr int CB = 16 * (2 / WC::EB);  // bf16 bytes a chunk fills in the stage
   auto stage_store = [&](int st) {
     char *base = s_kv + st * WC::STAGE;
+    if constexpr (KV == KV_FP8) {
+      if (tid < 2 * kSR) s_sc[st][tid / kSR][tid % kSR] = ssc;
+    }
     if (sall) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int ci = tid + kWThreads * i;
         if (!ALL && ci >= kSR * ROWCH) break;
         const int row = ci / ROWCH, col = ci % ROWCH;
-        *reinterpret_cast<uint4 *>(base + row * RSK + col * 16) = sk[i];
-        *reinterpret_cast<uint4 *>(base + kSR * RSK + row * RSV + col * 16) = sv[i];
+        put(base + row * RSK + col * CB, sk[i]);
+        put(base + kSR * RSK + row * RSV + col * CB, sv[i]);
       }
       return;
     }
@@ -542,10 +542,9 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       const int row = ci / ROWCH, col = ci % ROWCH;
       const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
                                                         // whole vector would go through memory
-      *reinterpret_cast<uint4 *>(base + row * RSK + col * 16) =
-          make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk);
-      *reinterpret_cast<uint4 *>(base + kSR * RSK + row * RSV + col * 16) =
-          make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk);
+      put(base + row * RSK + col * CB, make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk));
+      put(base + kSR * RSK + row * RSV + col * CB,
+          make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk));
     }
   };
 
@@ -558,6 +557,11 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     const bool full = ok[0] && ok[1] && (blk0 + 2) * kTok - 1 <= pfirst;
     const char *lk = s_kv + st * WC::STAGE + r0s * RSK;
     const char *lv = s_kv + st * WC::STAGE + kSR * RSK + r0s * RSV;
+    // FP8: scales of tokens 4q .. 4q+3 of block hb of the pair (read where
+    // used, which keeps the kernel within its 256 registers)
+    auto scales = [&](int which, int hb) {
+      return *reinterpret_cast<const float4 *>(&s_sc[KV == KV_FP8 ? st : 0][which][r0s + 16 * hb + 4 * q]);
+    };
     // A operands of S^T: token c of block hb, dims 32m + 8q .. +7
     uint4 kop[2][KM];
 #pragma unroll
@@ -600,9 +604,18 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
             s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[t0 + u][m], s[hb], 0, 0, 0);
         }
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        for (int hb = 0; hb < 2; ++hb) {
+          float ksc[4] = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (KV == KV_FP8) {
+            const float4 k4 = scales(0, hb);
+            ksc[0] = k4.x; ksc[1] = k4.y; ksc[2] = k4.z; ksc[3] = k4.w;
+          }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) x[u][hb][j] = s[hb][j] * sl2;
+          for (int j = 0; j < 4; ++j) {
+            x[u][hb][j] = s[hb][j] * sl2;
+            if constexpr (KV == KV_FP8) x[u][hb][j] *= ksc[j];
+          }
+        }
         mx[u] = max8(x[u]);
       }
       if (!full) {
@@ -666,10 +679,22 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
         // row c's tokens 4q .. 4q+3 of both blocks, the same k order as vb
         l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4[t], 0, 0, 0);
         l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4[t], 0, 0, 0);
+        bf16x8_t wh = ph, wl = pl;
+        if constexpr (KV == KV_FP8) {  // the V scale multiplies the PV weight
+          float pv[8];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const float4 v4 = scales(1, hb);
+            const float vsc[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pv[4 * hb + j] = pf[4 * hb + j] * vsc[j];  // masked: 0 x 0
+          }
+          split_bf16(pv, wh, wl);
+        }
 #pragma unroll
         for (int m = 0; m < EV; ++m) {
-          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb[m], o[t][m], 0, 0, 0);
-          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb[m], o[t][m], 0, 0, 0);
+          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vb[m], o[t][m], 0, 0, 0);
+          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vb[m], o[t][m], 0, 0, 0);
         }
       }
     }
@@ -717,27 +742,36 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 }
 
 
-template <int D, int G>
+template <int KV, int D, int G>
 hipError_t chunk_by_tiles(const ChunkArgs &a, unsigned grid, hipStream_t s) {
   if (a.nqt == 1) {
-    hipLaunchKernelGGL((chunk_kernel<D, G, 1>), dim3(grid), dim3(kCThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KV, D, G, 1>), dim3(grid), dim3(kCThreads), 0, s, a);
   } else if (a.nqt == 2) {
-    hipLaunchKernelGGL((chunk_kernel<D, G, 2>), dim3(grid), dim3(kCThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_kernel<KV, D, G, 2>), dim3(grid), dim3(kCThreads), 0, s, a);
   } else if (a.nqt == kWideRows / 16) {
-    hipLaunchKernelGGL((chunk_wide_kernel<D, G>), dim3(grid), dim3(kWThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_wide_kernel<KV, D, G>), dim3(grid), dim3(kWThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int KV, int D>
 hipError_t chunk_by_group(const ChunkArgs &a, unsigned grid, hipStream_t s) {
   switch (a.hq / a.hkv) {
-    case 1: return chunk_by_tiles<D, 1>(a, grid, s);
-    case 2: return chunk_by_tiles<D, 2>(a, grid, s);
-    case 4: return chunk_by_tiles<D, 4>(a, grid, s);
-    case 8: return chunk_by_tiles<D, 8>(a, grid, s);
+    case 1: return chunk_by_tiles<KV, D, 1>(a, grid, s);
+    case 2: return chunk_by_tiles<KV, D, 2>(a, grid, s);
+    case 4: return chunk_by_tiles<KV, D, 4>(a, grid, s);
+    case 8: return chunk_by_tiles<KV, D, 8>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KV>
+hipError_t chunk_by_dim(const ChunkArgs &a, unsigned grid, hipStream_t s) {
+  switch (a.d) {
+    case 64: return chunk_by_group<KV, 64>(a, grid, s);
+    case 128: return chunk_by_group<KV, 128>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -755,8 +789,9 @@ int chunk_items_per_head(int max_q, int group, int nqt) {
   return (int)((rows + 16LL * nqt - 1) / (16LL * nqt));
 }
 
-bool chunk_supported(int d, int group) {
-  return (d == 64 || d == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+bool chunk_supported(int kv, int d, int group) {
+  return (kv == KV_BF16 || kv == KV_FP8) && (d == 64 || d == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_chunk(const ChunkArgs &a, hipStream_t s) {
@@ -764,9 +799,9 @@ hipError_t launch_chunk(const ChunkArgs &a, hipStream_t s) {
   if (items == 0) return hipSuccess;
   if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)items;
-  switch (a.d) {
-    case 64: return chunk_by_group<64>(a, grid, s);
-    case 128: return chunk_by_group<128>(a, grid, s);
+  switch (a.kv) {
+    case KV_BF16: return chunk_by_dim<KV_BF16>(a, grid, s);
+    case KV_FP8: return chunk_by_dim<KV_FP8>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

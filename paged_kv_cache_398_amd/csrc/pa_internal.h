@@ -80,8 +80,10 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 // counted in items (sequence, KV head, tile of 16 * nqt query rows, a row
 // being one (query token, head of the group) pair).
 struct ChunkArgs {
-  const void *k_cache;      // [num_blocks][16][hkv][d] bf16
+  const void *k_cache;      // [num_blocks][16][hkv][d] bf16, or FP8 codes
   const void *v_cache;
+  const float *k_scale;     // [num_blocks][hkv][16] (FP8 only)
+  const float *v_scale;
   const void *q;            // [total_q][hq][d] bf16
   const int32_t *table;     // [batch][max_blocks]
   const int32_t *ctx;       // [batch]
@@ -93,6 +95,7 @@ struct ChunkArgs {
   int32_t nqt;              // 16-row tiles per item (1, 2, or 4 for d = 64)
   int32_t tiles;            // items per (sequence, KV head)
   float scale_log2e;        // softmax scale * log2(e)
+  int kv;                   // KvKind of the pool (KV_BF16 or KV_FP8)
 };
 
 // Tiles of 16 rows per item for a launch whose sequences have up to max_q
@@ -100,8 +103,8 @@ struct ChunkArgs {
 int chunk_tiles_per_item(int max_q, int group, int d);
 int chunk_items_per_head(int max_q, int group, int nqt);
 
-// True when the chunk kernel is built for (head_dim, group size).
-bool chunk_supported(int d, int group);
+// True when the chunk kernel is built for (pool kind, head_dim, group size).
+bool chunk_supported(int kv, int d, int group);
 
 // Enqueue the chunk kernel (one workgroup per item).
 hipError_t launch_chunk(const ChunkArgs &a, hipStream_t stream);

@@ -498,37 +498,6 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
 // rescale hands the row factors to the output layout through 16 floats of
 // per-wave LDS.
 
-template <int KV, int D>
-struct MCfg {
-  static constexpr int EB = KV == KV_FP8 ? 1 : 2;    // stored bytes per element
-  static constexpr int ROW = D * EB;                 // bytes of one head row in the pool
-  static constexpr int SEG = ROW < 128 ? ROW : 128;  // bytes of a row per load instruction
-  static constexpr int LPR = SEG / 16;               // lanes per row segment (16 B each)
-  static constexpr int RPI = 64 / LPR;               // rows per load instruction
-  static constexpr int NSEG = ROW / SEG;             // segments per row
-  static constexpr int NI = (16 / RPI) * NSEG;       // load instructions per block (K, and V)
-  static constexpr int KM = D / 32;                  // S^T products per block
-  static constexpr int EV = D / 16;                  // 16-dim slabs of O
-  static constexpr int RSK = D * 2 + 16;             // LDS row strides of the bf16 rows (bytes):
-  static constexpr int RSV = D * 2 + 32;             // K and V operand reads cover the banks once
-  static constexpr int TILE = 32 * (RSK + RSV);      // one pair: 32 K rows, then 32 V rows
-  static_assert(16 % RPI == 0 && ROW % SEG == 0, "whole rows per load instruction");
-};
-
-// A pair's loads in flight (registers), and what the compute needs of it.
-template <int KV, int D>
-struct PairLoads {
-  uint4 k[2][MCfg<KV, D>::NI], v[2][MCfg<KV, D>::NI];
-  float4 ks[2], vs[2];  // FP8: scales of tokens 4q .. 4q+3 of each block
-  int tok[2];           // sequence position of each block's slot 0
-  bool ok[2];           // block id inside the pool (no second block: false)
-};
-struct PairMeta {
-  float4 ks[2], vs[2];
-  int tok[2];
-  bool ok[2];
-};
-
 template <int KV, int D, int G>
 __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, int g, int tok0,
                                                   int tok_end, int ph, int nph, int w,
@@ -536,103 +505,18 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
                                                   float (*s_acc)[G][D], float (*s_m)[G],
                                                   float (*s_l)[G], char *tile, float *s_f) {
   using M = MCfg<KV, D>;
-  constexpr int NI = M::NI, KM = M::KM, EV = M::EV, RSK = M::RSK, RSV = M::RSV;
+  constexpr int KM = M::KM, EV = M::EV, RSK = M::RSK, RSV = M::RSV;
   const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
   const int blk0 = tok0 / kBlock;
   const int nb_w = wave_blocks(tok0, tok_end, ph, nph);
   const size_t block_bytes = (size_t)kBlock * a.hkv * M::ROW;
-  const char *kbase = static_cast<const char *>(a.k_cache);
-  const char *vbase = static_cast<const char *>(a.v_cache);
-
-  // this lane's row and offsets for load instruction ii: in the pool block
-  // (bytes), and in the bf16 tile row
-  int lrow[NI];
-  uint32_t loff[NI], toff[NI];
-#pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    lrow[ii] = (ii / M::NSEG) * M::RPI + lane / M::LPR;
-    const int byte = (ii % M::NSEG) * M::SEG + (lane % M::LPR) * 16;
-    loff[ii] = (uint32_t)((lrow[ii] * a.hkv + g) * M::ROW + byte);
-    toff[ii] = (uint32_t)(byte * (2 / M::EB));
-  }
-
-  // blocks i and i + 1 of the wave (ids id0, id1; -1 past the wave's blocks).
-  // Loads are unconditional (an id outside the pool reads block 0, masked
-  // when staged), so no branch around a load breaks the wait counting.
+  const StageLanes<KV, D> sl = stage_lanes<KV, D>(a.hkv, g);
   auto issue = [&](PairLoads<KV, D> &P, int i, int id0, int id1) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int id = hb ? id1 : id0;
-      P.tok[hb] = (blk0 + ph + (i + hb) * nph) * kBlock;
-      P.ok[hb] = (unsigned)id < (unsigned)a.num_blocks;
-      const size_t boff = P.ok[hb] ? (size_t)id * block_bytes : 0;
-#pragma unroll
-      for (int ii = 0; ii < NI; ++ii) {
-        if constexpr (KV == KV_FP8) {
-          P.k[hb][ii] = *reinterpret_cast<const uint4 *>(kbase + boff + loff[ii]);
-          P.v[hb][ii] = *reinterpret_cast<const uint4 *>(vbase + boff + loff[ii]);
-        } else {
-          P.k[hb][ii] = load_stream16(kbase + boff + loff[ii]);
-          P.v[hb][ii] = load_stream16(vbase + boff + loff[ii]);
-        }
-      }
-      if constexpr (KV == KV_FP8) {
-        const size_t si = ((P.ok[hb] ? (size_t)id : 0) * a.hkv + g) * kBlock + 4 * q;
-        P.ks[hb] = *reinterpret_cast<const float4 *>(a.k_scale + si);
-        P.vs[hb] = *reinterpret_cast<const float4 *>(a.v_scale + si);
-      }
-    }
+    issue_pair<KV, D>(P, sl, a.k_cache, a.v_cache, a.k_scale, a.v_scale, block_bytes, a.hkv, g,
+                      a.num_blocks, id0, id1, (blk0 + ph + i * nph) * kBlock,
+                      (blk0 + ph + (i + 1) * nph) * kBlock);
   };
-
-  // write a landed pair into the tile (bf16 rows; dead rows as zeros)
-  auto stage = [&](const PairLoads<KV, D> &P) {
-    PairMeta mt;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const bool all = P.ok[hb] && P.tok[hb] + kBlock <= tok_end;  // wave-uniform
-#pragma unroll
-      for (int ii = 0; ii < NI; ++ii) {
-        const bool live = all || (P.ok[hb] && P.tok[hb] + lrow[ii] < tok_end);
-        const uint32_t mk = live ? 0xFFFFFFFFu : 0u;
-        uint4 kx = P.k[hb][ii], vx = P.v[hb][ii];
-        if (!all) {
-          kx = make_uint4(kx.x & mk, kx.y & mk, kx.z & mk, kx.w & mk);
-          vx = make_uint4(vx.x & mk, vx.y & mk, vx.z & mk, vx.w & mk);
-        }
-        char *kd = tile + (16 * hb + lrow[ii]) * RSK + toff[ii];
-        char *vd = tile + 32 * RSK + (16 * hb + lrow[ii]) * RSV + toff[ii];
-        if constexpr (KV == KV_FP8) {
-          // 16 codes -> 16 bf16 (every E4M3FN value is a bf16 value)
-          auto widen = [](uint4 x, uint4 &lo, uint4 &hi) {
-            const uint32_t d[4] = {x.x, x.y, x.z, x.w};
-            uint32_t r[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              r[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], 1.0f, false));
-              r[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[j], 1.0f, true));
-            }
-            lo = make_uint4(r[0], r[1], r[2], r[3]);
-            hi = make_uint4(r[4], r[5], r[6], r[7]);
-          };
-          uint4 a0, a1;
-          widen(kx, a0, a1);
-          *reinterpret_cast<uint4 *>(kd) = a0;
-          *reinterpret_cast<uint4 *>(kd + 16) = a1;
-          widen(vx, a0, a1);
-          *reinterpret_cast<uint4 *>(vd) = a0;
-          *reinterpret_cast<uint4 *>(vd + 16) = a1;
-        } else {
-          *reinterpret_cast<uint4 *>(kd) = kx;
-          *reinterpret_cast<uint4 *>(vd) = vx;
-        }
-      }
-      mt.tok[hb] = P.tok[hb];
-      mt.ok[hb] = P.ok[hb];
-      mt.ks[hb] = P.ks[hb];
-      mt.vs[hb] = P.vs[hb];
-    }
-    return mt;
-  };
+  auto stage = [&](const PairLoads<KV, D> &P) { return stage_pair<KV, D>(P, sl, tile, tok_end); };
 
   float mrun = kNoMax;  // running max of query row c
   f32x4_t o[EV], l4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -718,12 +602,7 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
     const char *lv = tile + 32 * RSK;
 #pragma unroll
     for (int m = 0; m < EV; ++m) {
-      v4s_t h[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
-      const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8_t vb = v_operand_tr<D>(lv, RSV, m);
       o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vb, o[m], 0, 0, 0);
       o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vb, o[m], 0, 0, 0);
     }

@@ -1,10 +1,12 @@
 """GPU parity of the multi-token chunk attention (pa_chunk_run) with the oracle.
 
-Tolerance, from the kernel's arithmetic: q and K are bf16, so the products
-in the scores are exact and summed in fp32; each softmax weight enters the
-PV product as hi + lo, two bf16 values within a relative 2^-16 of it, and
-the normaliser sums the same hi + lo, so each output element is a convex
-combination of V values whose weights are off by at most a relative 2^-15:
+Tolerance, from the kernel's arithmetic: q and K are bf16 (FP8 codes are
+widened to bf16 exactly, and their per-token scales multiply the fp32
+scores), so the products in the scores are exact and summed in fp32; each
+softmax weight (times the V scale, for FP8) enters the PV product as hi + lo,
+two bf16 values within a relative 2^-16 of it, and the normaliser sums the
+same hi + lo of the weights, so each output element is a convex combination
+of V values whose weights are off by at most a relative 2^-15:
   |out - ref| <= 2^-15 * sum_t w_t |V_t| + 1e-4
 (the last term covers fp32 accumulation and the hardware exp2).  The bound
 is evaluated with the oracle itself, by running it on |V|.  Every case must
@@ -22,6 +24,8 @@ import oracle
 import paged_kv_cache_398_amd as pa
 from workloads import Spec, chunk_queries, make_chunk_inputs, make_inputs
 from workloads.device import to_device
+
+from gpu_util import host_threads as gpu_host_threads
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +47,7 @@ def gpu_chunk(ci, dev=None, extra_rows=0, q_start=None, max_q=None):
     out = torch.full((T + extra_rows, s.num_q_heads, s.head_dim), float("nan"),
                      dtype=torch.float32, device="cuda")
     qs = torch.from_numpy(ci.q_start if q_start is None else q_start).cuda()
-    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, "bf16")
+    pool = pa.PagedKVPool(dev.k_pool, dev.v_pool, s.kv_dtype, dev.k_scale, dev.v_scale)
     try:
         pool.set_block_table(dev.block_table, dev.context_lens, base.max_context_len)
         pool.chunk(_q_dev(ci), qs, ci.max_q_len if max_q is None else max_q, out,
@@ -55,11 +59,16 @@ def gpu_chunk(ci, dev=None, extra_rows=0, q_start=None, max_q=None):
 
 
 def oracle_chunk(ci, seqs=None, abs_v=False):
+    """The oracle's rows; with abs_v, over |V| (sign bits cleared: bf16 and
+    E4M3FN are sign-magnitude, and FP8 scales are positive)."""
     b = ci.base
-    v = (b.v_pool & np.uint16(0x7FFF)) if abs_v else b.v_pool
+    kv = b.spec.kv_dtype
+    v = b.v_pool
+    if abs_v:
+        v = v & (np.uint16(0x7FFF) if kv == "bf16" else np.uint8(0x7F))
     return oracle.paged_chunk_attention(ci.q, b.k_pool, v, b.block_table, b.context_lens,
-                                        ci.q_start, b.scale, kv_dtype="bf16", q_dtype="bf16",
-                                        seqs=seqs)
+                                        ci.q_start, b.scale, kv_dtype=kv, q_dtype="bf16",
+                                        k_scale=b.k_scale, v_scale=b.v_scale, seqs=seqs)
 
 
 REL = 2.0 ** -15  # relative error of the weights the kernel uses
@@ -88,9 +97,9 @@ def assert_parity(ci, got, seqs=None):
     return float(err.max()) if err.size else 0.0
 
 
-def _spec(name, d, hq, hkv, ctx, seed):
+def _spec(name, d, hq, hkv, ctx, seed, kv="bf16"):
     return Spec(name=name, batch=len(ctx), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
-                kv_dtype="bf16", q_dtype="bf16", seed=seed, context_lens=tuple(ctx))
+                kv_dtype=kv, q_dtype="bf16", seed=seed, context_lens=tuple(ctx))
 
 
 GROUPS = [(8, 8), (8, 4), (8, 2), (16, 2)]  # G = 1, 2, 4, 8
@@ -254,3 +263,66 @@ def test_chunk_prefill_full_size():
         say(f"  sequence {b}: max err {err.max():.2e}")
         assert np.all(err <= bound), (b, float(err.max()))
         assert err.max() <= 2e-3
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 caches (per-token, per-head scales): codes widened to bf16 in the
+# kernels' LDS tiles, the K scale on the score, the V scale on the weight
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 2), (16, 2)])
+def test_chunk_fp8_shapes(d, hq, hkv):
+    """Short chunks (16- and 32-row workgroups) and long ones (256 rows,
+    staged per 64 tokens): full prefills, chunks after a prefix, rows before
+    position zero, ragged tails; unused slots hold NaN codes and NaN scales."""
+    ctx = (1, 17, 40, 100, 700, 300, 5)
+    nq = (1, 5, 40, 7, 300, 129, 9)
+    base = make_inputs(_spec("chunk-fp8", d, hq, hkv, ctx, 1500 + d + hq + hkv, kv="fp8_e4m3"),
+                       poison=True)
+    for rows in (nq, tuple(min(n, 4) for n in nq)):
+        ci = chunk_queries(base, rows, 1600 + d + hq + rows[0])
+        say(f"[chunk] fp8 d={d} hq={hq} hkv={hkv} rows={ci.total_rows}")
+        err = assert_parity(ci, gpu_chunk(ci))
+        say(f"  max err {err:.2e}")
+
+
+@pytest.mark.parametrize("scale", [1.0, -0.3, 0.0])
+def test_chunk_fp8_scale_extremes(scale):
+    ctx = (1000, 300, 64)
+    base = dataclasses.replace(
+        make_inputs(_spec("chunk-fp8-scale", 128, 8, 2, ctx, 1700, kv="fp8_e4m3"), poison=True),
+        scale=np.float32(scale))
+    dev = to_device(base)
+    for nq in ((4, 4, 4), (40, 17, 5), (300, 260, 64)):
+        ci = chunk_queries(base, nq, 1710 + nq[0])
+        say(f"[chunk] fp8 scale={scale} rows/seq={nq}")
+        err = assert_parity(ci, gpu_chunk(ci, dev=dev))
+        say(f"  max err {err:.2e}")
+
+
+def test_chunk_fp8_spec_verify_full_size():
+    """Speculative verification (4 rows per sequence: 3 drafts and the last
+    accepted token) over the full FP8 MHA cache (32 sequences of 8192 tokens,
+    32 KV heads): every row against the oracle, sequences checked
+    concurrently."""
+    from concurrent.futures import ThreadPoolExecutor
+    from workloads import NAMED_SPECS
+    base = make_inputs(NAMED_SPECS["fp8_mha_b32_ctx8k"])
+    ci = chunk_queries(base, [4] * base.spec.batch, 1800)
+    say(f"[chunk] fp8 spec verify full size, rows={ci.total_rows}")
+    got = gpu_chunk(ci)
+    assert np.all(np.isfinite(got))
+    B = base.spec.batch
+    jobs = [(b, absv) for b in range(B) for absv in (False, True)]
+    with ThreadPoolExecutor(max_workers=gpu_host_threads()) as ex:
+        res = dict(zip(jobs, ex.map(lambda j: oracle_chunk(ci, [j[0]], abs_v=j[1]), jobs)))
+    worst = 0.0
+    for b in range(B):
+        r = rows_of(ci, [b])
+        want, bound = res[(b, False)][r], REL * res[(b, True)][r] + 1e-4
+        err = np.abs(got[r] - want)
+        worst = max(worst, float(err.max()))
+        assert np.all(err <= bound), (b, float(err.max()))
+    say(f"  max err {worst:.2e}")
+    assert worst <= 2e-3
