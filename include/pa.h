@@ -303,15 +303,17 @@ pa_status pa_bm_stats(const pa_block_manager *bm, int32_t *free_blocks, int32_t 
  *   k_params: device fp16 [num_blocks][num_kv_heads][2][head_dim] -- per
  *     channel of the block: scale (row 0) and min (row 1); 16-byte aligned.
  *   v_params: device fp16 [num_blocks][num_kv_heads][16][2] -- per token:
- *     (scale, min); 4-byte aligned.  value = code * scale + min.
+ *     (scale, min); 16-byte aligned.  value = code * scale + min.
  *   Errors: PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED.
  * pa_kivi_residual_set -- the bf16 rows of each sequence's partly filled
  *   last block: device [batch][16][num_kv_heads][head_dim] (row b belongs to
- *   sequence b of the tables set last; slot t % 16 holds token t).  Tokens
- *   of full blocks are read through the table, the last context_lens % 16
- *   tokens from here.  Errors: PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE.
+ *   sequence b of the tables set last; slot t % 16 holds token t), 16-byte
+ *   aligned.  Tokens of full blocks are read through the table, the last
+ *   context_lens % 16 tokens from here.  Errors: PA_ERR_NULL, PA_ERR_DTYPE,
+ *   PA_ERR_SHAPE.
  * pa_decode_kivi_run -- one decode step over such a pool: q bf16
- *   [batch][num_q_heads][head_dim], out float32.  No workspace.  Errors as
+ *   [batch][num_q_heads][head_dim] (16-byte aligned), out float32.  No
+ *   workspace.  Errors as
  *   pa_decode_run, plus PA_ERR_STATE without a residual.
  * pa_cache_append on such a pool takes bf16 rows: the new token goes to its
  *   residual row; the token that fills a block (t % 16 == 15) has the block

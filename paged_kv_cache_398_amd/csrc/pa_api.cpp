@@ -529,8 +529,8 @@ pa_status pa_kv_pool_create_kivi(int32_t num_blocks, int32_t num_kv_heads, int32
   if ((int64_t)num_kv_heads * head_dim * 4 * PA_BLOCK_SIZE > (int64_t)1 << 30)
     return fail(PA_ERR_SHAPE, "num_kv_heads too large");
   if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_params, 16) ||
-      !aligned(v_params, 4))
-    return fail(PA_ERR_SHAPE, "codes and K parameters must be 16-byte aligned, V parameters 4");
+      !aligned(v_params, 16))
+    return fail(PA_ERR_SHAPE, "codes and parameters must be 16-byte aligned");
   pa_kv_pool *p = new (std::nothrow) pa_kv_pool();
   if (!p) return fail(PA_ERR_SHAPE, "out of host memory");
   p->num_blocks = num_blocks;
@@ -551,8 +551,8 @@ pa_status pa_kivi_residual_set(pa_kv_pool *pool, void *res_k, void *res_v) {
   if (!pool->kivi_bits) return fail(PA_ERR_DTYPE, "only INT8/INT4 pools have a residual");
   if ((res_k == nullptr) != (res_v == nullptr))
     return fail(PA_ERR_NULL, "res_k and res_v must both be set or both be NULL");
-  if (res_k && (!aligned(res_k, 4) || !aligned(res_v, 4)))
-    return fail(PA_ERR_SHAPE, "the residual must be 4-byte aligned");
+  if (res_k && (!aligned(res_k, 16) || !aligned(res_v, 16)))
+    return fail(PA_ERR_SHAPE, "the residual must be 16-byte aligned");
   pool->res_k = res_k;
   pool->res_v = res_v;
   return ok();
@@ -574,6 +574,8 @@ pa_status pa_decode_kivi_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
   if (pool->batch == 0) return ok();
   if (!q || !out) return fail(PA_ERR_NULL, "q or out is NULL");
   if (!pool->res_k) return fail(PA_ERR_STATE, "no residual set (pa_kivi_residual_set)");
+  if (!aligned(q, 16)) return fail(PA_ERR_SHAPE, "q must be 16-byte aligned");
+  if (!aligned(out, 4)) return fail(PA_ERR_SHAPE, "out must be 4-byte aligned");
   if ((size_t)pool->batch * pool->num_kv_heads >= (size_t(1) << 31))
     return fail(PA_ERR_SHAPE, "batch * num_kv_heads too large");
   const pa::KiviArgs a = kivi_args(pool, q, num_q_heads, scale, out);

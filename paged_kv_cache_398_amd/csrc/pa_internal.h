@@ -118,7 +118,7 @@ hipError_t launch_attention(const LaunchArgs &a, hipStream_t stream);
 // An INT8 / INT4 pool quantised the KIVI way (codes, fp16 parameters) with
 // the bf16 residual of each sequence's partly filled last block.
 struct KiviArgs {
-  void *k_codes, *v_codes;  // [num_blocks][16][hkv][d * bits / 8]
+  void *k_codes, *v_codes;  // [num_blocks][hkv][16][d * bits / 8] (head-major)
   void *k_par;              // fp16 [num_blocks][hkv][2][d]: scales, then mins
   void *v_par;              // fp16 [num_blocks][hkv][16][2]: (scale, min) per slot
   void *res_k, *res_v;      // bf16 [batch][16][hkv][d]

@@ -382,3 +382,34 @@ def test_status_strings_of_the_block_manager():
     lib = pa.load_library()
     assert lib.pa_status_str(8) == b"no free block"
     assert lib.pa_status_str(9) == b"unknown or duplicate sequence"
+
+
+def test_kivi_pool_errors():
+    """INT8/INT4 pools: dtype, shape and 16-byte alignment of codes, both
+    parameter arrays, the residual and q (the kernel reads all of them with
+    16-byte loads), and the order of the calls."""
+    c = pa.pa_kv_pool_create_kivi
+    P1, P2 = 0x90000, 0xA0000
+    assert _status(c, 8, 2, 128, "bf16", K, V, P1, P2) == pa.binding.PA_ERR_DTYPE
+    assert _status(c, 8, 2, 128, "int8_kivi", K, None, P1, P2) == pa.binding.PA_ERR_NULL
+    assert _status(c, 0, 2, 128, "int8_kivi", K, V, P1, P2) == pa.binding.PA_ERR_SHAPE
+    assert _status(c, 8, 2, 96, "int4_kivi", K, V, P1, P2) == pa.binding.PA_ERR_UNSUPPORTED
+    for bad in [(K + 8, V, P1, P2), (K, V, P1 + 4, P2), (K, V, P1, P2 + 4)]:
+        assert _status(c, 8, 2, 128, "int4_kivi", *bad) == pa.binding.PA_ERR_SHAPE
+        assert "16-byte" in pa.pa_last_error()
+    h = c(8, 2, 128, "int4_kivi", K, V, P1, P2)
+    try:
+        pa.pa_block_table_set(h, TBL, CTX, 3, 4, 64)
+        # no residual yet
+        assert _status(pa.pa_decode_kivi_run, h, Q, "bf16", 8, 0.1, OUT, 0) == pa.binding.PA_ERR_STATE
+        assert _status(pa.pa_kivi_residual_set, h, 0xB0004, 0xC0000) == pa.binding.PA_ERR_SHAPE
+        assert _status(pa.pa_kivi_residual_set, h, 0xB0000, None) == pa.binding.PA_ERR_NULL
+        pa.pa_kivi_residual_set(h, 0xB0000, 0xC0000)
+        assert _status(pa.pa_decode_kivi_run, h, Q + 8, "bf16", 8, 0.1, OUT, 0) == pa.binding.PA_ERR_SHAPE
+        assert _status(pa.pa_decode_kivi_run, h, Q, "f32", 8, 0.1, OUT, 0) == pa.binding.PA_ERR_DTYPE
+        assert _status(pa.pa_decode_kivi_run, h, Q, "bf16", 6, 0.1, OUT, 0) == pa.binding.PA_ERR_UNSUPPORTED
+        assert _status(pa.pa_decode_kivi_run, h, Q, "bf16", 7, 0.1, OUT, 0) == pa.binding.PA_ERR_SHAPE
+        # the bf16 entry points refuse an INT pool
+        assert _status(pa.pa_decode_run, h, Q, "bf16", 8, 0.1, OUT, WS, 1 << 20, 0) == pa.binding.PA_ERR_DTYPE
+    finally:
+        pa.pa_kv_pool_destroy(h)

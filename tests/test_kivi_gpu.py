@@ -3,8 +3,10 @@
 * Decode (pa_decode_kivi_run) against oracle.kivi_decode_attention: all
   group sizes, head_dim 64 and 128, both widths, lengths with and without a
   residual (0, 1, 15, 16, 17, ...), table entries past the used blocks
-  poisoned; tolerance 2e-3 (fp32 arithmetic on exact codes and fp16
-  parameters, as for the bf16 path).
+  poisoned; tolerance 2e-3, the decode bar.  The kernel multiplies the
+  exact codes on the matrix cores against q * scale and p * scale each held
+  as two bf16 terms (within 2^-16 relative); on the Llama-3-8B-shaped pool
+  (sharp softmax, |K| up to ~15) that leaves ~1.5e-4.
 * Cache write (pa_cache_append on such a pool) against oracle.kivi_append:
   residual rows, codes and fp16 parameters byte for byte, both for tokens
   that fill their block (quantisation) and for those that do not.
