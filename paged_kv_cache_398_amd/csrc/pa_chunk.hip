@@ -360,9 +360,6 @@ constexpr int kWThreads = kWW * 64;
 constexpr int kWideRows = kWW * kWT * 16; // rows per workgroup
 constexpr int kSB = 4;                    // blocks per LDS stage (two pairs)
 constexpr int kSR = kSB * 16;             // token rows per stage
-// tiles per softmax phase: as many as the registers allow without spilling
-template <int D>
-constexpr int phase_tiles() { return D == 64 ? kWT : 1; }
 
 template <int KV, int D>
 struct WideCfg {
@@ -390,7 +387,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   using WC = WideCfg<KV, D>;
   constexpr int KM = C::KM, EV = C::EV;
   constexpr int RSK = WC::RSK, RSV = WC::RSV, NCH = WC::NCH, ROWCH = WC::ROWCH;
-  constexpr int kPH = phase_tiles<D>();
+  constexpr int kPH = kWT;  // tiles per softmax phase: all of the wave's
   static_assert(kWT % kPH == 0, "whole phases");
   constexpr bool ALL = WC::ALL;
   __shared__ __align__(16) char s_kv[2 * WC::STAGE];
@@ -465,6 +462,29 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   // Slots past the cached tokens and blocks outside the pool are stored as
   // zeros: their scores are masked anyway, and V garbage (NaN) cannot leak
   // into the products.
+  // What a thread's chunks are is the same in every stage, so it is worked
+  // out once: chunk i is row ci / ROWCH, 16-byte column ci % ROWCH of the
+  // stage (ci = tid + 512 i); its block of the stage, ci / (16 ROWCH), is
+  // the same for the whole wave (a wave's 64 chunks never straddle two
+  // blocks), so the block id is a scalar.
+  constexpr int CB = 16 * (2 / WC::EB);  // bf16 bytes a chunk fills in the stage
+  uint32_t c_src[NCH];  // bytes into a pool block: (slot, head g, column)
+  uint32_t c_dst[NCH];  // bytes into a stage: the K row's column (V: + c_vdst[i])
+  uint32_t c_vdst[NCH];
+  int c_slot[NCH], c_hb[NCH];
+  bool c_live[NCH];  // the chunk exists (not every thread has NCH of them)
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int ci = tid + kWThreads * i;
+    c_live[i] = ALL || ci < kSR * ROWCH;
+    const int cc = c_live[i] ? ci : 0;
+    const int row = cc / ROWCH, col = cc % ROWCH;
+    c_slot[i] = row & 15;
+    c_hb[i] = __builtin_amdgcn_readfirstlane((w * 64 + kWThreads * i) / (16 * ROWCH));
+    c_src[i] = (uint32_t)((c_slot[i] * a.hkv + g) * WC::ROWB + col * 16);
+    c_dst[i] = (uint32_t)(row * RSK + col * CB);
+    c_vdst[i] = (uint32_t)(kSR * RSK + row * RSV + col * CB);
+  }
   uint4 sk[NCH], sv[NCH];
   bool sreal[NCH];
   bool sall = true;  // every slot of the stage real (wave-uniform)
@@ -480,18 +500,15 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + kWThreads * i;
-      if (!ALL && ci >= kSR * ROWCH) break;
-      const int row = ci / ROWCH, col = ci % ROWCH;
-      const int hb = row >> 4, slot = row & 15;
+      if (!c_live[i]) break;
       int bid = id[0];
 #pragma unroll
-      for (int h = 1; h < kSB; ++h) bid = hb == h ? id[h] : bid;
+      for (int h = 1; h < kSB; ++h) bid = c_hb[i] == h ? id[h] : bid;
       const bool ok = (unsigned)bid < (unsigned)a.num_blocks;
-      sreal[i] = ok && (blk0 + hb) * kTok + slot < n_ctx;
-      const size_t off = (ok ? (size_t)bid * block_bytes : 0) + (size_t)((slot * a.hkv + g) * WC::ROWB + col * 16);
-      sk[i] = *reinterpret_cast<const uint4 *>(kbase + off);
-      sv[i] = *reinterpret_cast<const uint4 *>(vbase + off);
+      sreal[i] = ok && (blk0 + c_hb[i]) * kTok + c_slot[i] < n_ctx;
+      const size_t boff = ok ? (size_t)bid * block_bytes : 0;
+      sk[i] = *reinterpret_cast<const uint4 *>(kbase + boff + c_src[i]);
+      sv[i] = *reinterpret_cast<const uint4 *>(vbase + boff + c_src[i]);
     }
     if constexpr (KV == KV_FP8) {
       if (tid < 2 * kSR) {
@@ -518,7 +535,6 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       *reinterpret_cast<uint4 *>(dst) = x;
     }
   };
-  constexpr int CB = 16 * (2 / WC::EB);  // bf16 bytes a chunk fills in the stage
   auto stage_store = [&](int st) {
     char *base = s_kv + st * WC::STAGE;
     if constexpr (KV == KV_FP8) {
@@ -527,24 +543,19 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     if (sall) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int ci = tid + kWThreads * i;
-        if (!ALL && ci >= kSR * ROWCH) break;
-        const int row = ci / ROWCH, col = ci % ROWCH;
-        put(base + row * RSK + col * CB, sk[i]);
-        put(base + kSR * RSK + row * RSV + col * CB, sv[i]);
+        if (!c_live[i]) break;
+        put(base + c_dst[i], sk[i]);
+        put(base + c_vdst[i], sv[i]);
       }
       return;
     }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + kWThreads * i;
-      if (!ALL && ci >= kSR * ROWCH) break;
-      const int row = ci / ROWCH, col = ci % ROWCH;
+      if (!c_live[i]) break;
       const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
                                                         // whole vector would go through memory
-      put(base + row * RSK + col * CB, make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk));
-      put(base + kSR * RSK + row * RSV + col * CB,
-          make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk));
+      put(base + c_dst[i], make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk));
+      put(base + c_vdst[i], make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk));
     }
   };
 
@@ -569,22 +580,6 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 #pragma unroll
       for (int m = 0; m < KM; ++m)
         kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + (16 * hb + c) * RSK + (32 * m + 8 * q) * 2);
-    // B operands of O = P V, one per 16 dims (slab m): lane (n = c, q)
-    // needs V[token 4q + e of block hb][dim 16m + n] for e = 0..3, hb = 0, 1.
-    // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of
-    // the 8 bytes addressed by lanes 4r + i / 4, r = 0..3 (checked on the
-    // GPU with a one-wave probe); so lane 4r + s addresses token 4q + r,
-    // dims 16m + 4s .. 16m + 4s + 3, of the row-major V rows in LDS.
-    bf16x8_t vb[EV];
-#pragma unroll
-    for (int m = 0; m < EV; ++m) {
-      v4s_t h[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
-      vb[m] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
     // the tiles in groups of kPH: all score products of a group first, then
     // the softmax of all its tiles with one (rarely taken) rescaling branch,
     // then all PV products -- a single basic block in the common case, so
@@ -663,6 +658,24 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
             for (int m = 0; m < EV; ++m) o[t][m][r] *= fr[r];
           }
         }
+      }
+      // B operands of O = P V, one per 16 dims (slab m): lane (n = c, q)
+      // needs V[token 4q + e of block hb][dim 16m + n] for e = 0..3, hb = 0, 1.
+      // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of
+      // the 8 bytes addressed by lanes 4r + i / 4, r = 0..3 (checked on the
+      // GPU with a one-wave probe); so lane 4r + s addresses token 4q + r,
+      // dims 16m + 4s .. 16m + 4s + 3, of the row-major V rows in LDS.
+      // (read after the score products, so that these registers and the K
+      // operands' are not live at once)
+      bf16x8_t vb[EV];
+#pragma unroll
+      for (int m = 0; m < EV; ++m) {
+        v4s_t h[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
+        vb[m] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int u = 0; u < kPH; ++u) {
