@@ -34,7 +34,11 @@ METRIC = "paged decode attention KV-read TB/s, % of 8 TB/s HBM peak; µs per dec
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_398_amd", "csrc", f)
                for f in ("pa_kernels.hip", "pa_internal.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_kernel_llama3_8b_b32_ctx4k.json")
+
+
+def traffic_file(workload):
+    """Committed HBM-counter figures of the attention kernel on ``workload``."""
+    return os.path.join(ROOT, "profiles", f"traffic_attention_kernel_{workload}.json")
 
 
 def log(msg):
@@ -64,7 +68,7 @@ def stored_traffic(workload):
     committed counter runs, if taken on that workload with the current
     kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
