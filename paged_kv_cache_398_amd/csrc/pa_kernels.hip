@@ -474,7 +474,9 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
 }
 
 // ---------------------------------------------------------------------------
-// The matrix-core form of a wave's share of a piece (bf16 and FP8 pools).
+// The matrix-core form of a wave's share of a piece (bf16 pools; f32 and
+// FP8 pools take the vector-ALU form above, which measured faster for FP8's
+// half-width rows).
 //
 // A wave takes its blocks two at a time (a pair: 32 tokens).  Each load
 // instruction covers whole 128-byte pieces of 8 token rows (16 bytes per
@@ -492,8 +494,7 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
 //    lane (n, q) receives dim 16m + n of those tokens); lane (n, q) then
 //    holds O[rows 4q .. 4q+3][16m + n].  The weights enter as hi + lo bf16
 //    (two products, within a relative 2^-16 of the fp32 weights); the row
-//    sums come from the same two products against a ones operand.  FP8: the
-//    K scale multiplies the score, the V scale the weight of the PV product.
+//    sums come from the same two products against a ones operand.
 // The running max is per query row (lanes (c, *)), lagged by kTau; its rare
 // rescale hands the row factors to the output layout through 16 floats of
 // per-wave LDS.
@@ -504,6 +505,7 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
                                                   const Query<KV, D, G> &qry, int tv0,
                                                   float (*s_acc)[G][D], float (*s_m)[G],
                                                   float (*s_l)[G], char *tile, float *s_f) {
+  static_assert(KV == KV_BF16, "the matrix-core form reads bf16 pools");
   using M = MCfg<KV, D>;
   constexpr int KM = M::KM, EV = M::EV, RSK = M::RSK, RSV = M::RSV;
   const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
@@ -541,14 +543,9 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
                       mt.tok[1] + kBlock <= tok_end;  // wave-uniform
     float x[2][4];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const float kscale[4] = {mt.ks[hb].x, mt.ks[hb].y, mt.ks[hb].z, mt.ks[hb].w};
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[hb][j] = sc[hb][j] * sl2;
-        if constexpr (KV == KV_FP8) x[hb][j] *= kscale[j];
-      }
-    }
+      for (int j = 0; j < 4; ++j) x[hb][j] = sc[hb][j] * sl2;
     if (!full) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -584,27 +581,12 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
     split_bf16(pf, ph, pl);
     l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4, 0, 0, 0);
     l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4, 0, 0, 0);
-    bf16x8_t wh = ph, wl = pl;
-    if constexpr (KV == KV_FP8) {
-      float pv[8];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const float vscale[4] = {mt.vs[hb].x, mt.vs[hb].y, mt.vs[hb].z, mt.vs[hb].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float t = pf[4 * hb + j] * vscale[j];
-          // a dead slot's scale may be anything (NaN included): its weight is 0
-          pv[4 * hb + j] = full || (mt.ok[hb] && mt.tok[hb] + 4 * q + j < tok_end) ? t : 0.f;
-        }
-      }
-      split_bf16(pv, wh, wl);
-    }
     const char *lv = tile + 32 * RSK;
 #pragma unroll
     for (int m = 0; m < EV; ++m) {
       const bf16x8_t vb = v_operand_tr<D>(lv, RSV, m);
-      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vb, o[m], 0, 0, 0);
-      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vb, o[m], 0, 0, 0);
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[m], 0, 0, 0);
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[m], 0, 0, 0);
     }
   };
 
