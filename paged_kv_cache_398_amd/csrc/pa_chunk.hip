@@ -16,14 +16,17 @@
 //
 //  - chunk_kernel, up to 32 rows per item (short chunks, speculative
 //    verification): the four waves split the item's visible blocks in pairs
-//    (wave w takes pairs w, w + 4, ...), loading K/V straight into
-//    registers, and are combined exactly in LDS at the end;
+//    (wave w takes pairs w, w + 4, ...), each staging its pairs through a
+//    per-wave LDS tile as the decode kernel's matrix-core form does (loads
+//    covering whole 128-byte pieces of 8 token rows, FP8 codes widened to
+//    bf16 on the way, exactly), and are combined exactly in LDS at the end;
 //  - chunk_wide_kernel, 256 rows per item (long prefill chunks): eight
-//    waves each own 32 rows for the whole context, and every pair of blocks
-//    is staged once per workgroup in LDS, from where all of them read it.
+//    waves each own 32 rows for the whole visible context, and every 64
+//    tokens are staged once per workgroup in LDS, from where all of them
+//    read their operands.
 //
 // In both, the products run on the matrix cores (v_mfma_f32_16x16x32_bf16),
-// transposed so that every lane holds one query row throughout:
+// laid out so that every lane holds one query row's scores:
 //
 //  - S^T = K Q^T per block: A = K (row = token, lane % 16; k = 8 dims,
 //    lane / 16), B = Q^T (column = query row, lane % 16), D/32 products
@@ -33,20 +36,14 @@
 //    FlashAttention sections of the pages) is lane-local apart from a
 //    4-lane max; the running max is raised only when a pair's maximum
 //    exceeds it by more than kLag (log2 units), so rescaling is rare.
-//  - O^T += V^T P^T over a pair of blocks (32 tokens): B = P^T in bf16,
-//    lane (row c, k = 8 tokens: 4q..4q+3 of each block), which is exactly
-//    the lane's own probabilities; A = V^T, lane (dim row, same 8 tokens).
-//    Each lane loads the V rows 4q..4q+3 of both blocks at dims EV*c ..
-//    EV*c + EV - 1 (whole 16- or 8-byte slices, every row read in full by
-//    16 lanes) and the EV products take element m of each: product m covers
-//    dims EV*rho + m, rho = 0..15.  The accumulator then gives lane (c, q)
-//    dims 4*EV*q .. 4*EV*q + 4*EV - 1 of row c.  The V^T operands are
-//    built by byte permutes once per pair, shared by the row tiles.  (The
-//    wide kernel instead computes O = P V with A = the same P registers and
-//    B = V read from LDS by transposing reads, no permutes; a lane then
-//    holds one dimension of four rows.)
-//  - The row sums l come out of the matrix cores too: one more product per
-//    tile with A = all ones gives every lane the sum of its row's weights.
+//  - O = P V over a pair of blocks (32 tokens): A = P, lane (row c, k = 8
+//    tokens: 4q..4q+3 of each block), exactly the lane's own weights; B = V
+//    read from the bf16 rows in LDS by transposing reads (ds_read_b64_tr_b16:
+//    lane (n, q) receives dim 16m + n of those tokens).  A lane then holds
+//    one dimension of rows 4q .. 4q+3 of its tile.
+//  - The row sums l come out of the matrix cores too: the same weights
+//    against an all-ones operand give every lane its rows' sums.
+//  - FP8 pools: the K scale multiplies the score, the V scale the weight.
 //
 // Probabilities enter the PV product as a sum of two bf16 values, hi (the
 // probability truncated to bf16) and lo (the remainder rounded to bf16):
@@ -55,10 +52,9 @@
 // convex combination of V rows whose weights are off by at most a relative
 // 2^-15.  (One bf16 product, a relative 2^-9 per weight, gave errors up to
 // 2.8e-3 on contexts of a few tokens.)  Positions past a row's own, and
-// blocks or table entries
-// outside the pool, contribute exactly nothing: their scores are replaced by
-// -inf and the V rows of slots past the cached tokens by zeros (selects, not
-// products, so NaN garbage there cannot leak).
+// blocks or table entries outside the pool, contribute exactly nothing:
+// their scores are replaced by -inf and the V rows of slots past the cached
+// tokens by zeros (selects, not products, so NaN garbage there cannot leak).
 
 #include "pa_internal.h"
 #include "pa_mfma.h"
@@ -76,9 +72,8 @@ constexpr float kNoMax = -3.402823466e38f;
 
 template <int D>
 struct ChunkCfg {
-  static constexpr int KM = D / 32;   // S^T products per block (32 dims each)
-  static constexpr int EV = D / 16;   // V elements per lane per token row
-  static constexpr int VDW = EV / 2;  // dwords of that slice
+  static constexpr int KM = D / 32;  // S^T products per block (32 dims each)
+  static constexpr int EV = D / 16;  // 16-dim slabs of O (one PV product each)
 };
 
 template <int KV, int D, int G, int NQT>
