@@ -126,31 +126,12 @@ __device__ __forceinline__ uint2 widen_u8x4(uint32_t w) {
                     bf16_pair((float)((w >> 16) & 0xFF), (float)(w >> 24)));
 }
 
-// x & 0x0F0F0F0F, opaque to the compiler: were the zero upper nibbles known,
-// it would replace each byte-to-float conversion below by a bit-field
-// extract and a conversion.
-__device__ __forceinline__ uint32_t low_nibbles(uint32_t x) {
-  uint32_t r;
-  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-
 // (x & m) | c in one instruction (both constants in registers: a VOP3
 // instruction takes no literal here).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
   return r;
-}
-
-// 8 INT4 codes -> 8 bf16, channel order kept (nibbles spread to bytes first,
-// so that each is one byte-to-float conversion).
-__device__ __forceinline__ uint4 widen_u4x8(uint32_t w) {
-  const uint32_t e = low_nibbles(w), o = low_nibbles(w >> 4);
-  return make_uint4(bf16_pair((float)(e & 0xFF), (float)(o & 0xFF)),
-                    bf16_pair((float)((e >> 8) & 0xFF), (float)((o >> 8) & 0xFF)),
-                    bf16_pair((float)((e >> 16) & 0xFF), (float)((o >> 16) & 0xFF)),
-                    bf16_pair((float)(e >> 24), (float)(o >> 24)));
 }
 
 // 8 INT4 codes -> bf16 of 128 + code, as pairs of channels (0,4), (1,5),
