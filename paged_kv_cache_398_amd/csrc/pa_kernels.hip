@@ -890,17 +890,26 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
       if (whole) {
         a.out[(bh0 + r) * D + e] = L > 0.f ? A / L : 0.f;
       } else {
-        a.ws_acc[(rec0 + r) * D + e] = A;
-        if (e == 0) a.ws_ml[rec0 + r] = make_float2(M, L);
+        // device-coherent stores: see the arrival below
+        __hip_atomic_store(&a.ws_acc[(rec0 + r) * D + e], A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (e == 0) {
+          float *ml = reinterpret_cast<float *>(&a.ws_ml[rec0 + r]);
+          __hip_atomic_store(ml, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ml + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
 
     if (!whole) {
-      // Arrival.  Each wave waits until its own stores have reached the L2
-      // (the barrier by itself does not wait for outstanding stores); thread
-      // 0's device-scope release then covers them all.  The arrival that
-      // completes the count acquires every earlier one (one release
-      // sequence on the counter) and the barrier hands that on.
+      // Arrival.  The record was stored with device-coherent (write-through)
+      // stores, and each wave waits until its own stores are complete (the
+      // barrier by itself does not wait for outstanding stores), so the
+      // record is in device-coherent memory before thread 0 counts the
+      // arrival; a release on the counter would add a write-back of the
+      // whole L2, which measured 2% of the continuous-batch step.  The
+      // arrival that completes the count takes a device-scope acquire
+      // (its L2 is invalidated, so its loads of the records fetch them
+      // afresh) and the barrier hands that on.
       // The pair's counter is indexed by the first workgroup it touches: a
       // range holds the first unit of at most one pair that runs past its
       // end, so no two split pairs share a counter.
@@ -909,7 +918,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE,
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         const bool last = old == (uint32_t)(w_hi - w_lo);
         if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
