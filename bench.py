@@ -453,6 +453,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20,
                     help="timed steps of each other named decode workload, and of the "
                          "main workload with K and V in separate allocations (0: skip)")
+    ap.add_argument("--warm-ms", type=float, default=300.0,
+                    help="untimed steps for at least this long before the timed ones")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -505,10 +507,20 @@ def main():
         pools[i % R].decode(dev.q, out, ws, scale=scale)
 
     # every pool runs once before the warm-up steps, so that no first use of
-    # a pool falls inside the timed region whatever --warmup is
+    # a pool falls inside the timed region whatever --warmup is; then more
+    # untimed steps until --warm-ms of them have run, so that the timed
+    # region does not start while the GPU's clocks still ramp up from the
+    # idle of the input generation
     for i in range(R + args.warmup):
         step(i)
     torch.cuda.synchronize()
+    warm_runs = R + args.warmup
+    t_w = time.perf_counter()
+    while (time.perf_counter() - t_w) * 1e3 < args.warm_ms:
+        for i in range(R):
+            step(i)
+        torch.cuda.synchronize()
+        warm_runs += R
     # HIP events around the kernels of the steps that use pool 0 (every R-th
     # step of the timed region): recording them on every step would itself
     # add several microseconds between back-to-back launches.
@@ -630,7 +642,7 @@ def main():
             "layers_cycled": R, "kv_heads_per_workgroup": hc,
             "kv_placement": "K and V pools of a layer in one buffer, V at a 2 KiB "
                             "boundary + 256 B (pa_kv_pool_placement)",
-            "untimed_runs_before_timing": R + args.warmup,
+            "untimed_runs_before_timing": warm_runs,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
