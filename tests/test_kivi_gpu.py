@@ -231,3 +231,44 @@ def test_kivi_full_size_llama_step(bits):
     err = float(np.abs(got - want).max())
     say(f"[kivi] full size bits={bits}: max abs err {err:.2e} over all {s.batch} sequences")
     assert err <= 2e-3
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kivi_invalid_block_ids_are_skipped(bits):
+    """Out-of-range ids (negative, and >= num_blocks) among a sequence's full
+    blocks -- its first blocks, one in the middle, every one of them -- add
+    nothing: the output equals the oracle over the remaining blocks and the
+    residual (decode attention depends on the set of cached tokens, not on
+    their positions).  The kernel reads block 0 in place of an invalid id,
+    so nothing is read out of bounds."""
+    rng = np.random.Generator(np.random.PCG64(4400 + bits))
+    hq, hkv, d = 8, 2, 128
+    lens = [300, 100, 64, 17, 1000]
+    N = sum(n // BLOCK for n in lens) + 3
+    kc, vc, kp, vp, rk, rv = kivi_state(rng, N, len(lens), hkv, d, bits)
+    width = max(n // BLOCK for n in lens) + 2
+    table = _table(rng, lens, N, width)
+    q = _bf16_bits(rng.standard_normal((len(lens), hq, d)))
+    drops = {0: (0, 1, 2, 3, 4, 5, 6, 7, 8, 9), 1: (3,), 2: (0, 1, 2, 3), 4: (10, 11, 40)}
+    ids = [-1, N, N + 1000, -7, 2 ** 31 - 1, N + 1, -100, N + 5]
+    bad = table.copy()
+    kept = np.full_like(table, -1)
+    kept_lens = np.array(lens)
+    for b, n in enumerate(lens):
+        js = drops.get(b, ())
+        for i, j in enumerate(js):
+            bad[b, j] = ids[i % len(ids)]
+        keep = [j for j in range(n // BLOCK) if j not in js]
+        kept[b, :len(keep)] = table[b, keep]
+        kept_lens[b] -= BLOCK * len(js)
+    say(f"[kivi] invalid ids bits={bits}")
+    g = Gpu(kc, vc, kp, vp, rk, rv, bits)
+    try:
+        g.tables(bad, lens, max(lens))
+        got = g.decode(q, hq, float(np.float32(1 / np.sqrt(d))))
+    finally:
+        g.close()
+    want = kivi.kivi_decode_attention(q, kc, vc, kp, vp, rk, rv, kept, kept_lens,
+                                      np.float32(1 / np.sqrt(d)), bits)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - want).max() <= 2e-3
