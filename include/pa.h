@@ -398,9 +398,11 @@ pa_status pa_decode_workspace_clear(void *workspace, size_t workspace_bytes, voi
  *   allocation; runs leave it zero); the rest is scratch.  May be NULL when
  *   that size is 0.  Runs that overlap in time must not share a workspace.
  * stream: hipStream_t of the caller.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE (pool is FP8, or q_dtype
- *   does not match), PA_ERR_UNSUPPORTED (group size), PA_ERR_STATE (no
- *   table set), PA_ERR_WORKSPACE, PA_ERR_HIP (launch failed; out undefined).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (also when batch * num_kv_heads *
+ *   ceil(max_context_len / 16) reaches 2^30: the kernel counts its work in
+ *   32-bit integers), PA_ERR_DTYPE (pool is FP8, or q_dtype does not
+ *   match), PA_ERR_UNSUPPORTED (group size), PA_ERR_STATE (no table set),
+ *   PA_ERR_WORKSPACE, PA_ERR_HIP (launch failed; out undefined).
  */
 pa_status pa_decode_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
                         int32_t num_q_heads, float scale, float *out, void *workspace,

@@ -209,6 +209,10 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
   }
   if ((size_t)pool->batch * hq >= (size_t(1) << 31))
     return fail(PA_ERR_SHAPE, "batch * num_q_heads too large");
+  // the kernel counts its work (16-token blocks of one (sequence, head
+  // chunk)) in 32-bit integers, with headroom for its range arithmetic
+  if (max_units(pool, 1) >= (int64_t(1) << 30))
+    return fail(PA_ERR_SHAPE, "batch * num_kv_heads * ceil(max_context_len / 16) must be below 2^30");
   if (pool->batch == 0) return ok();
 
   // ---- from here on HIP is used (launches only: no allocation, no wait)

@@ -499,24 +499,57 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
 // rescale hands the row factors to the output layout through 16 floats of
 // per-wave LDS.
 
+// The loads of the wave's blocks i and i + 1 (ids id0, id1) of a piece whose
+// first block is blk0: blocks blk0 + ph + i * nph and blk0 + ph + (i + 1) * nph
+// of the sequence, KV head g.
+template <int KV, int D>
+__device__ __forceinline__ void issue_piece_pair(const LaunchArgs &a, const StageLanes<KV, D> &sl,
+                                                 int g, int blk0, int ph, int nph,
+                                                 PairLoads<KV, D> &P, int i, int id0, int id1) {
+  const size_t block_bytes = (size_t)kBlock * a.hkv * MCfg<KV, D>::ROW;
+  issue_pair<KV, D>(P, sl, a.k_cache, a.v_cache, a.k_scale, a.v_scale, block_bytes, a.hkv, g,
+                    a.num_blocks, id0, id1, (blk0 + ph + i * nph) * kBlock,
+                    (blk0 + ph + (i + 1) * nph) * kBlock);
+}
+
+// The first loads of a wave's share of a piece (its first two pairs), as
+// attend_piece_mfma issues them; the kernel issues them early for the piece
+// it guesses, before the scan of the lengths, and hands A and B over with
+// pre = true.  tv0: the table entries of the wave's first 64 blocks.
+template <int KV, int D>
+__device__ __forceinline__ void issue_first_pairs(const LaunchArgs &a, int g, int tok0,
+                                                  int tok_end, int ph, int nph, int tv0,
+                                                  PairLoads<KV, D> &A, PairLoads<KV, D> &B) {
+  const int nb_w = wave_blocks(tok0, tok_end, ph, nph);
+  if (nb_w == 0) return;
+  const int blk0 = tok0 / kBlock;
+  const StageLanes<KV, D> sl = stage_lanes<KV, D>(a.hkv, g);
+  issue_piece_pair<KV, D>(a, sl, g, blk0, ph, nph, A, 0, __builtin_amdgcn_readlane(tv0, 0),
+                          __builtin_amdgcn_readlane(tv0, 1));
+  if (nb_w > 2)
+    issue_piece_pair<KV, D>(a, sl, g, blk0, ph, nph, B, 2, __builtin_amdgcn_readlane(tv0, 2),
+                            __builtin_amdgcn_readlane(tv0, 3));
+}
+
+// A and B hold the pairs in flight; with pre, the first two pairs' loads were
+// issued into them already (issue_first_pairs, same arguments).
 template <int KV, int D, int G>
 __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, int g, int tok0,
                                                   int tok_end, int ph, int nph, int w,
                                                   const Query<KV, D, G> &qry, int tv0,
                                                   float (*s_acc)[G][D], float (*s_m)[G],
-                                                  float (*s_l)[G], char *tile, float *s_f) {
+                                                  float (*s_l)[G], char *tile, float *s_f,
+                                                  PairLoads<KV, D> &A, PairLoads<KV, D> &B,
+                                                  bool pre) {
   static_assert(KV == KV_BF16, "the matrix-core form reads bf16 pools");
   using M = MCfg<KV, D>;
   constexpr int KM = M::KM, EV = M::EV, RSK = M::RSK, RSV = M::RSV;
   const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
   const int blk0 = tok0 / kBlock;
   const int nb_w = wave_blocks(tok0, tok_end, ph, nph);
-  const size_t block_bytes = (size_t)kBlock * a.hkv * M::ROW;
   const StageLanes<KV, D> sl = stage_lanes<KV, D>(a.hkv, g);
   auto issue = [&](PairLoads<KV, D> &P, int i, int id0, int id1) {
-    issue_pair<KV, D>(P, sl, a.k_cache, a.v_cache, a.k_scale, a.v_scale, block_bytes, a.hkv, g,
-                      a.num_blocks, id0, id1, (blk0 + ph + i * nph) * kBlock,
-                      (blk0 + ph + (i + 1) * nph) * kBlock);
+    issue_piece_pair<KV, D>(a, sl, g, blk0, ph, nph, P, i, id0, id1);
   };
   auto stage = [&](const PairLoads<KV, D> &P) { return stage_pair<KV, D>(P, sl, tile, tok_end); };
 
@@ -599,9 +632,10 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
     const int tv = c0 == 0 ? tv0 : load_table(a, b, blk0, ph, nph, c0, nb_w);
     auto entry = [&](int i) { return __builtin_amdgcn_readlane(tv, i); };  // i < 64
     const int np = (cn + 1) / 2;
-    PairLoads<KV, D> A, B;
-    issue(A, c0, entry(0), entry(1));
-    if (np > 1) issue(B, c0 + 2, entry(2), entry(3));
+    if (c0 > 0 || !pre) {
+      issue(A, c0, entry(0), entry(1));
+      if (np > 1) issue(B, c0 + 2, entry(2), entry(3));
+    }
     int p = 0;
     for (; p + 3 < np; p += 2) {
       const PairMeta ma = stage(A);
@@ -645,40 +679,43 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
 // one, every weight is 1 and the sum stays 0.
 __device__ __forceinline__ float part_weight(float m, float M) { return fast_exp2(m - M); }
 
-// Sum over the workgroup (int64), every thread gets the result.
-__device__ __forceinline__ long long block_sum(long long x, long long *part) {
+// Sum over the workgroup, every thread gets the result.
+__device__ __forceinline__ int block_sum(int x, int *part) {
 #pragma unroll
   for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
   __syncthreads();
-  long long r = 0;
+  int r = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) r += part[i];
   return r;
 }
 
-// Inclusive prefix sum over the workgroup (int64); *total gets the sum.
-__device__ __forceinline__ long long block_scan(long long x, long long *part, long long *total) {
+// Inclusive prefix sum over the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_scan(int x, int *part, int *total) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off *= 2) {
-    const long long y = __shfl_up(x, off);
+    const int y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
   __syncthreads();
   if (lane == 63) part[threadIdx.x >> 6] = x;
   __syncthreads();
-  long long before = 0, all = 0;
+  int before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    const long long v = part[i];
+    const int v = part[i];
     if (i < (int)(threadIdx.x >> 6)) before += v;
     all += v;
   }
   *total = all;
   return x + before;
 }
+
+// Quotient of non-negative ints (unsigned division: the shorter sequence).
+__device__ __forceinline__ int udiv(int x, int y) { return (int)((unsigned)x / (unsigned)y); }
 
 // ---------------------------------------------------------------------------
 // attention kernel
@@ -701,8 +738,8 @@ template <int KV, int D, int G>
 __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G], s_l[kWaves][G];
-  __shared__ long long s_scan[kWaves];
-  __shared__ long long s_first[3];  // first sequence, its first unit, its length
+  __shared__ int s_scan[kWaves];
+  __shared__ int s_first[3];  // first sequence, its first unit, its length
   __shared__ int s_len[kThreads];     // clamped lengths, when batch <= kThreads
   __shared__ int s_last;
   // per-wave staging tiles and rescale factors of the matrix-core form
@@ -713,9 +750,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   // wave index, known wave-uniform: everything derived from it stays scalar
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwg = gridDim.x, wgi = blockIdx.x;
-  // head chunk of an equal-length batch (a.hc): the speculation below uses it
-  const int hc0 = a.hc;
-  const int nph0 = kWaves / hc0, hl0 = w % hc0, ph0 = w / hc0;
+  // head chunk of an equal-length batch (a.hc): the speculation below uses it.
+  // Head chunks are powers of two dividing kWaves.
+  const int hc0 = a.hc, lhc0 = __builtin_ctz(hc0);
+  const int nph0 = kWaves >> lhc0, hl0 = w & (hc0 - 1), ph0 = w >> lhc0;
 
   auto seq_len = [&](int b) { return min(max(a.ctx[b], 0), a.max_ctx); };
   auto seq_blocks = [&](int b) { return (seq_len(b) + kBlock - 1) / kBlock; };
@@ -727,22 +765,32 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   // is max_ctx long (an equal-length batch).  Its query rows and table
   // entries are loaded now, in flight together with the lengths the split
   // below needs, and used if the lengths confirm the guess.
+  // Unit counts and indices are 32-bit: the host rejects a launch whose
+  // batch * num_kv_heads * ceil(max_ctx / 16) reaches 2^31.  (64-bit
+  // divisions expand to long instruction sequences, which held back every
+  // workgroup's first loads by microseconds.)
   const int nbm = (a.max_ctx + kBlock - 1) / kBlock;
-  const long long Ug = (long long)a.batch * a.chunks * nbm;
+  const int Ug = a.batch * a.chunks * nbm;
   Query<KV, D, G> qry_g;
   int tv_g = -1;
+  bool guess = false;  // the guessed piece: KV head g_g, tokens [tok0_g, tok_end_g)
+  int g_g = 0, tok0_g = 0, tok_end_g = 0;
   {
-    const long long per_g = Ug / nwg, rem_g = Ug % nwg;
-    const long long u0g = wgi * per_g + min((long long)wgi, rem_g);
-    const long long u1g = u0g + per_g + (wgi < rem_g ? 1 : 0);
+    const int per_g = udiv(Ug, nwg), rem_g = Ug - per_g * nwg;
+    const int u0g = wgi * per_g + min(wgi, rem_g);
+    const int u1g = u0g + per_g + (wgi < rem_g ? 1 : 0);
     if (u0g < u1g) {
-      const int bg = (int)(u0g / ((long long)a.chunks * nbm));
-      const long long off = u0g - (long long)bg * a.chunks * nbm;
-      const int cg = (int)(off / nbm), lo = (int)(off % nbm);
-      const int hi = (int)min((long long)nbm, u1g - (long long)bg * a.chunks * nbm - (long long)cg * nbm);
-      load_query<KV, D, G>(a, bg, cg * hc0 + hl0, qry_g);
-      tv_g = load_table(a, bg, lo, ph0, nph0, 0,
-                        wave_blocks(lo * kBlock, min(a.max_ctx, hi * kBlock), ph0, nph0));
+      const int seq_units = a.chunks * nbm;
+      const int bg = udiv(u0g, seq_units);
+      const int off = u0g - bg * seq_units;
+      const int cg = udiv(off, nbm), lo = off - cg * nbm;
+      const int hi = min(nbm, u1g - bg * seq_units - cg * nbm);
+      guess = true;
+      g_g = cg * hc0 + hl0;
+      tok0_g = lo * kBlock;
+      tok_end_g = min(a.max_ctx, hi * kBlock);
+      load_query<KV, D, G>(a, bg, g_g, qry_g);
+      tv_g = load_table(a, bg, lo, ph0, nph0, 0, wave_blocks(tok0_g, tok_end_g, ph0, nph0));
     }
   }
 
@@ -751,47 +799,50 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   // u0.  Up to kThreads sequences: one block-wide scan of the per-sequence
   // blocks gives all of them.  More: a sum, then a chunked scan below.
   if (tid == 0) s_first[0] = -1;
-  long long TB, incl_b = 0;
+  int TB, incl_b = 0;
   int my_len = 0;
+  if (small_batch) my_len = tid < a.batch ? seq_len(tid) : 0;
+  // Matrix-core form: the guessed piece's first KV loads go out as soon as
+  // its table entries land, in flight during the scan below (unused when
+  // the guess fails; every address is inside the pools).
+  PairLoads<KV, D> pA, pB;
+  if constexpr (uses_mfma<KV>()) {
+    if (guess) issue_first_pairs<KV, D>(a, g_g, tok0_g, tok_end_g, ph0, nph0, tv_g, pA, pB);
+  }
   if (small_batch) {
-    my_len = tid < a.batch ? seq_len(tid) : 0;
     s_len[tid] = my_len;
     incl_b = block_scan((my_len + kBlock - 1) / kBlock, s_scan, &TB);
   } else {
-    long long t = 0;
+    int t = 0;
     for (int b = tid; b < a.batch; b += kThreads) t += seq_blocks(b);
     TB = block_sum(t, s_scan);
   }
   // The head chunk: a.hc when every sequence has max_ctx's block count (the
   // equal-length batch the host sized it for), else a.hc_var.  No sequence
   // has more blocks than max_ctx, so that is exactly TB == batch * nbm.
-  const bool full = __builtin_amdgcn_readfirstlane((int)(TB == (long long)a.batch * nbm)) != 0;
-  const int hc = full ? a.hc : a.hc_var;
-  const int chunks = a.hkv / hc;
-  const int nph = kWaves / hc;  // phases: waves sharing a head
-  const int hl = w % hc, ph = w / hc;
+  const bool full = __builtin_amdgcn_readfirstlane((int)(TB == a.batch * nbm)) != 0;
+  const int hc = full ? a.hc : a.hc_var, lhc = __builtin_ctz(hc);
+  const int chunks = a.hkv >> lhc;
+  const int nph = kWaves >> lhc;  // phases: waves sharing a head
+  const int hl = w & (hc - 1), ph = w >> lhc;
   const int hcg = hc * G;       // query heads of a chunk
-  const long long U = TB * chunks;
+  const int U = TB * chunks;
+  const int per = udiv(U, nwg), rem = U - per * nwg;
+  auto range_start = [&](int wg) { return wg * per + min(wg, rem); };
+  auto range_of = [&](int u) {  // workgroup whose range holds unit u
+    const int big = rem * (per + 1);
+    return u < big ? udiv(u, per + 1) : rem + udiv(u - big, per);
+  };
+  const int u0 = range_start(wgi), u1 = range_start(wgi + 1);
   if (small_batch) {
-    const long long ub = (long long)((my_len + kBlock - 1) / kBlock) * chunks;
-    const long long incl = incl_b * chunks;
-    if (ub > 0) {
-      const long long per = U / nwg, rem = U % nwg;
-      const long long u0 = wgi * per + min((long long)wgi, rem);
-      if (incl - ub <= u0 && u0 < incl) {
-        s_first[0] = tid;
-        s_first[1] = incl - ub;
-        s_first[2] = my_len;
-      }
+    const int ub = ((my_len + kBlock - 1) / kBlock) * chunks;
+    const int incl = incl_b * chunks;
+    if (ub > 0 && incl - ub <= u0 && u0 < incl) {
+      s_first[0] = tid;
+      s_first[1] = incl - ub;
+      s_first[2] = my_len;
     }
   }
-  const long long per = U / nwg, rem = U % nwg;
-  auto range_start = [&](long long wg) { return wg * per + min(wg, rem); };
-  auto range_of = [&](long long u) {  // workgroup whose range holds unit u
-    const long long big = rem * (per + 1);
-    return u < big ? u / (per + 1) : rem + (u - big) / per;
-  };
-  const long long u0 = range_start(wgi), u1 = range_start(wgi + 1);
 
   // empty sequences: zero output rows, spread over the workgroups (done
   // after this workgroup's pieces, off the path to its first loads)
@@ -808,13 +859,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   }
 
   if (a.batch > kThreads) {
-    long long base = 0;
+    int base = 0;
     for (int c0 = 0; c0 < a.batch; c0 += kThreads) {
       const int b = c0 + tid;
-      const long long ub = b < a.batch ? (long long)seq_blocks(b) * chunks : 0;
-      long long total;
-      const long long incl = block_scan(ub, s_scan, &total);
-      const long long start = base + incl - ub;
+      const int ub = b < a.batch ? seq_blocks(b) * chunks : 0;
+      int total;
+      const int incl = block_scan(ub, s_scan, &total);
+      const int start = base + incl - ub;
       if (ub > 0 && start <= u0 && u0 < start + ub) {
         s_first[0] = b;
         s_first[1] = start;
@@ -826,16 +877,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     }
   }
   __syncthreads();
-  int b = (int)s_first[0];
-  long long pb = s_first[1];  // first unit of sequence b
-  int n = (int)s_first[2];    // its length (the scan has read it already)
+  int b = s_first[0];
+  int pb = s_first[1];  // first unit of sequence b
+  int n = s_first[2];   // its length (the scan has read it already)
 
   // ---- the pieces of the range
-  long long pos = u0;
+  int pos = u0;
   bool first_piece = true;
   while (pos < u1) {
     const int nb = (n + kBlock - 1) / kBlock;
-    const long long ub = (long long)nb * chunks;
+    const int ub = nb * chunks;
     if (ub == 0) {  // an empty sequence inside the range holds no units
       ++b;
       n = len_of(b);
@@ -843,31 +894,32 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     }
     // the next sequence's length, read now and used after this piece
     const int n_next = b + 1 < a.batch ? len_of(b + 1) : 0;
-    const long long off = pos - pb;
-    const int chunk = (int)(off / nb);
-    const int blk_lo = (int)(off - (long long)chunk * nb);
-    const long long seg_start = pb + (long long)chunk * nb, seg_end = seg_start + nb;
-    const long long pend = min(u1, seg_end);
-    const int blk_hi = (int)(pend - seg_start);
+    const int off = pos - pb;
+    const int chunk = udiv(off, nb);
+    const int blk_lo = off - chunk * nb;
+    const int seg_start = pb + chunk * nb, seg_end = seg_start + nb;
+    const int pend = min(u1, seg_end);
+    const int blk_hi = pend - seg_start;
 
     const int g = chunk * hc + hl;
     const int tok0 = blk_lo * kBlock, tok_end = min(n, blk_hi * kBlock);
     // the guess holds when every sequence has max_ctx tokens' worth of
     // blocks and this one exactly max_ctx tokens: then the first piece is
     // the guessed one, same blocks and same tail
-    auto piece = [&](const Query<KV, D, G> &qr, int tvr) {
+    auto piece = [&](const Query<KV, D, G> &qr, int tvr, bool pre) {
       if constexpr (uses_mfma<KV>())
         attend_piece_mfma<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qr, tvr, s_acc, s_m, s_l,
-                                    s_tile + (uses_mfma<KV>() ? w * MCfg<KV, D>::TILE : 0), s_fw[w]);
+                                    s_tile + (uses_mfma<KV>() ? w * MCfg<KV, D>::TILE : 0), s_fw[w],
+                                    pA, pB, pre);
       else
         attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qr, tvr, s_acc, s_m, s_l);
     };
     if (first_piece && full && U == Ug && n == a.max_ctx) {
-      piece(qry_g, tv_g);
+      piece(qry_g, tv_g, true);
     } else {
       Query<KV, D, G> qry;
       load_query<KV, D, G>(a, b, g, qry);
-      piece(qry, load_table(a, b, blk_lo, ph, nph, 0, wave_blocks(tok0, tok_end, ph, nph)));
+      piece(qry, load_table(a, b, blk_lo, ph, nph, 0, wave_blocks(tok0, tok_end, ph, nph)), false);
     }
     __syncthreads();
 
@@ -913,7 +965,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
       // The pair's counter is indexed by the first workgroup it touches: a
       // range holds the first unit of at most one pair that runs past its
       // end, so no two split pairs share a counter.
-      const long long w_lo = range_of(seg_start), w_hi = range_of(seg_end - 1);
+      const int w_lo = range_of(seg_start), w_hi = range_of(seg_end - 1);
       uint32_t *cnt = a.counters + w_lo;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();

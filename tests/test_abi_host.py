@@ -122,6 +122,18 @@ def test_run_errors(pool):
         pa.binding.PA_ERR_WORKSPACE
 
 
+def test_run_refuses_unit_counts_past_32_bits(pool):
+    """The kernel counts (sequence, KV head, 16-token block) units in 32-bit
+    integers: a launch with batch * num_kv_heads * ceil(max_context_len / 16)
+    at 2^30 or more is refused before any HIP call."""
+    batch, max_blocks = 1 << 14, 1 << 15  # * 2 KV heads = 2^30 units
+    pa.pa_block_table_set(pool, TBL, CTX, batch, max_blocks, 16 * max_blocks)
+    ws = pa.pa_decode_workspace_bytes(pool, 8)
+    assert _status(pa.pa_decode_run, pool, Q, "bf16", 8, 0.1, OUT, WS, ws, 0) == \
+        pa.binding.PA_ERR_SHAPE
+    assert "2^30" in pa.pa_last_error()
+
+
 def test_fp8_pool_needs_fp8_entry():
     h = pa.pa_kv_pool_create(64, 16, 4, 128, "fp8_e4m3", K, V, KS, VS)
     try:
