@@ -679,13 +679,23 @@ __device__ __forceinline__ void attend_piece_mfma(const LaunchArgs &a, int b, in
 // one, every weight is 1 and the sum stays 0.
 __device__ __forceinline__ float part_weight(float m, float M) { return fast_exp2(m - M); }
 
+// A workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load the wave has in flight (its release fence
+// waits for all vector memory operations), which would stall the early KV
+// loads of the prologue; the barriers there only publish LDS data.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over the workgroup, every thread gets the result.
 __device__ __forceinline__ int block_sum(int x, int *part) {
 #pragma unroll
   for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_barrier();
   int r = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) r += part[i];
@@ -700,9 +710,9 @@ __device__ __forceinline__ int block_scan(int x, int *part, int *total) {
     const int y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
-  __syncthreads();
+  lds_barrier();
   if (lane == 63) part[threadIdx.x >> 6] = x;
-  __syncthreads();
+  lds_barrier();
   int before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
@@ -871,12 +881,12 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
         s_first[1] = start;
         s_first[2] = seq_len(b);
       }
-      __syncthreads();
+      lds_barrier();
       base += total;
       if (s_first[0] >= 0) break;
     }
   }
-  __syncthreads();
+  lds_barrier();
   int b = s_first[0];
   int pb = s_first[1];  // first unit of sequence b
   int n = s_first[2];   // its length (the scan has read it already)
@@ -930,14 +940,26 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
     for (int idx = tid; idx < hcg * D; idx += kThreads) {
       const int r = idx / D, e = idx % D;  // r = hl * G + hh
       const int hh = r % G, hw = r / G;
+      // the waves of head hw are hw, hw + hc, ... (nph of them); every
+      // part's values are read at once (a part past nph re-reads part 0 and
+      // gets weight 0, which leaves the sums exactly those of the nph parts)
+      float mv[kWaves], lv[kWaves], av[kWaves];
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const int wv = (v < nph ? v : 0) * hc + hw;
+        mv[v] = s_m[wv][hh];
+        lv[v] = s_l[wv][hh];
+        av[v] = s_acc[wv][hh][e];
+      }
       float M = kNoMax;
-      for (int v = 0; v < nph; ++v) M = fmaxf(M, s_m[v * hc + hw][hh]);
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, mv[v]);
       float A = 0.f, L = 0.f;
-      for (int v = 0; v < nph; ++v) {
-        const int wv = v * hc + hw;
-        const float sc = part_weight(s_m[wv][hh], M);
-        A = fmaf(sc, s_acc[wv][hh][e], A);
-        L = fmaf(sc, s_l[wv][hh], L);
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float sc = v < nph ? part_weight(mv[v], M) : 0.f;
+        A = fmaf(sc, av[v], A);
+        L = fmaf(sc, lv[v], L);
       }
       if (whole) {
         a.out[(bh0 + r) * D + e] = L > 0.f ? A / L : 0.f;
