@@ -783,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
   const int Ug = a.batch * a.chunks * nbm;
   Query<KV, D, G> qry_g;
   int tv_g = -1;
-  bool guess = false;  // the guessed piece: KV head g_g, tokens [tok0_g, tok_end_g)
+  bool guess = false;  // early loads for the guessed piece: KV head g_g, tokens [tok0_g, tok_end_g)
   int g_g = 0, tok0_g = 0, tok_end_g = 0;
   {
     const int per_g = udiv(Ug, nwg), rem_g = Ug - per_g * nwg;
@@ -795,7 +795,9 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
       const int off = u0g - bg * seq_units;
       const int cg = udiv(off, nbm), lo = off - cg * nbm;
       const int hi = min(nbm, u1g - bg * seq_units - cg * nbm);
-      guess = true;
+      // worth loading early only if the guessed sequence has the full
+      // length (its length lands in the same round trip as the table)
+      guess = seq_len(bg) == a.max_ctx;
       g_g = cg * hc0 + hl0;
       tok0_g = lo * kBlock;
       tok_end_g = min(a.max_ctx, hi * kBlock);
@@ -925,7 +927,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(LaunchArgs a) {
         attend_piece<KV, D, G>(a, b, g, tok0, tok_end, ph, nph, w, qr, tvr, s_acc, s_m, s_l);
     };
     if (first_piece && full && U == Ug && n == a.max_ctx) {
-      piece(qry_g, tv_g, true);
+      piece(qry_g, tv_g, guess);  // guess: its first pairs are in flight
     } else {
       Query<KV, D, G> qry;
       load_query<KV, D, G>(a, b, g, qry);
