@@ -25,8 +25,9 @@
 //    tokens are staged once per workgroup in LDS, from where all of them
 //    read their operands.
 //
-// In both, the products run on the matrix cores (v_mfma_f32_16x16x32_bf16),
-// laid out so that every lane holds one query row's scores:
+// In both, the products run on the matrix cores (v_mfma_f32_16x16x32_bf16,
+// and _f16 for the wide kernel's PV products over bf16 pools), laid out so
+// that every lane holds one query row's scores:
 //
 //  - S^T = K Q^T per block: A = K (row = token, lane % 16; k = 8 dims,
 //    lane / 16), B = Q^T (column = query row, lane % 16), D/32 products
@@ -51,13 +52,22 @@
 // probability.  The normaliser l sums the same hi + lo, so the output is a
 // convex combination of V rows whose weights are off by at most a relative
 // 2^-15.  (One bf16 product, a relative 2^-9 per weight, gave errors up to
-// 2.8e-3 on contexts of a few tokens.)  Positions past a row's own, and
+// 2.8e-3 on contexts of a few tokens.)  The wide kernel over bf16 pools
+// instead stages V as fp16 (exact for bf16 magnitudes in [2^-14, 65504];
+// below that an absolute error under 2^-24, above it saturated) and rounds
+// each probability to the nearest fp16 (a relative 2^-11): one
+// v_mfma_f32_16x16x32_f16 per slab, weights off by at most a relative
+// 2^-10.  Its staging threads convert V once per stage for all 256 rows.
+// FP8 pools keep the two bf16 terms: the V scale multiplies the weight,
+// which could leave fp16's range.  Positions past a row's own, and
 // blocks or table entries outside the pool, contribute exactly nothing:
 // their scores are replaced by -inf and the V rows of slots past the cached
 // tokens by zeros (selects, not products, so NaN garbage there cannot leak).
 
 #include "pa_internal.h"
 #include "pa_mfma.h"
+
+#include <type_traits>
 
 namespace pa {
 namespace {
@@ -445,6 +455,9 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   }
   const float sl2 = a.scale_log2e;
   const bf16x8_t ones = bf16x8_ones();
+  const f16x8_t ones16 = f16x8_ones();
+  // the type of the staged V rows and PV operands: fp16 over bf16 pools
+  using VOp = std::conditional_t<KV == KV_BF16, f16x8_t, bf16x8_t>;
 
   const int *trow = a.table + (size_t)b * a.max_blocks;
   const size_t block_bytes = (size_t)kTok * a.hkv * WC::ROWB;
@@ -530,6 +543,14 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       *reinterpret_cast<uint4 *>(dst) = x;
     }
   };
+  // V rows: fp16 over bf16 pools (the PV products take fp16 operands there),
+  // as put() over FP8 pools
+  auto put_v = [&](char *dst, uint4 x) {
+    if constexpr (KV == KV_BF16)
+      *reinterpret_cast<uint4 *>(dst) = bf16x8_to_f16x8(x);
+    else
+      put(dst, x);
+  };
   auto stage_store = [&](int st) {
     char *base = s_kv + st * WC::STAGE;
     if constexpr (KV == KV_FP8) {
@@ -540,7 +561,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       for (int i = 0; i < NCH; ++i) {
         if (!c_live[i]) break;
         put(base + c_dst[i], sk[i]);
-        put(base + c_vdst[i], sv[i]);
+        put_v(base + c_vdst[i], sv[i]);
       }
       return;
     }
@@ -550,7 +571,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       const uint32_t mk = sreal[i] ? 0xFFFFFFFFu : 0u;  // per word: a select of the
                                                         // whole vector would go through memory
       put(base + c_dst[i], make_uint4(sk[i].x & mk, sk[i].y & mk, sk[i].z & mk, sk[i].w & mk));
-      put(base + c_vdst[i], make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk));
+      put_v(base + c_vdst[i], make_uint4(sv[i].x & mk, sv[i].y & mk, sv[i].z & mk, sv[i].w & mk));
     }
   };
 
@@ -662,7 +683,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       // dims 16m + 4s .. 16m + 4s + 3, of the row-major V rows in LDS.
       // (read after the score products, so that these registers and the K
       // operands' are not live at once)
-      bf16x8_t vb[EV];
+      VOp vb[EV];
 #pragma unroll
       for (int m = 0; m < EV; ++m) {
         v4s_t h[2];
@@ -670,7 +691,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
         for (int hb = 0; hb < 2; ++hb)
           h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
-        vb[m] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        vb[m] = __builtin_bit_cast(VOp, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int u = 0; u < kPH; ++u) {
@@ -681,10 +702,21 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) pf[4 * hb + j] = __builtin_amdgcn_exp2f(x[u][hb][j] + nm);
+        // O = P V: lane (c, q)'s eight weights are row c's tokens 4q .. 4q+3
+        // of both blocks, the same k order as vb
+        if constexpr (KV == KV_BF16) {
+          // bf16 pools: fp16 weights (within a relative 2^-11) and fp16 V,
+          // one product per slab; the row sums from the same fp16 weights
+          const f16x8_t p16 = to_f16x8(pf);
+          l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, ones16, l4[t], 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < EV; ++m)
+            o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, vb[m], o[t][m], 0, 0, 0);
+          continue;
+        }
+        // FP8 pools: the weights as hi + lo bf16, two products per slab
         bf16x8_t ph, pl;
         split_bf16(pf, ph, pl);
-        // O = P V with A = P (hi, then lo): lane (c, q)'s eight weights are
-        // row c's tokens 4q .. 4q+3 of both blocks, the same k order as vb
         l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4[t], 0, 0, 0);
         l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4[t], 0, 0, 0);
         bf16x8_t wh = ph, wl = pl;

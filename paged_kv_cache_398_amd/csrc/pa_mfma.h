@@ -1,8 +1,9 @@
 // pa_mfma.h -- device helpers shared by the kernels that run their products
-// on the matrix cores (v_mfma_f32_16x16x32_bf16): operand types, the 4-lane
-// maximum of a 16x16 result column, the two-term bf16 split of the softmax
-// weights, and the staged loads of K/V block pairs into a per-wave LDS
-// tile.  Internal; included by the .hip sources only.
+// on the matrix cores (v_mfma_f32_16x16x32_bf16 and _f16): operand types,
+// the 4-lane maximum of a 16x16 result column, the two-term bf16 split of
+// the softmax weights and their fp16 rounding, and the staged loads of K/V
+// block pairs into a per-wave LDS tile.  Internal; included by the .hip
+// sources only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +19,38 @@ typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// fp16 operands (v_mfma_f32_16x16x32_f16): the wide chunk kernel's PV
+// products over bf16 pools take fp16 weights and fp16 V.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// 1.0 in all eight fp16 lanes
+__device__ __forceinline__ f16x8_t f16x8_ones() {
+  return __builtin_bit_cast(f16x8_t, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+}
+
+// Eight fp32 values rounded to the nearest fp16 (a relative 2^-11 for the
+// softmax weights, which lie in (0, 2^8]; below 2^-24 they become 0).
+__device__ __forceinline__ f16x8_t to_f16x8(const float (&p)[8]) {
+  f16x8_t h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (_Float16)p[e];
+  return h;
+}
+
+// Eight bf16 values (16 bytes) as fp16: exact for magnitudes in
+// [2^-14, 65504]; rounded toward zero below that (an absolute error under
+// 2^-24) and above it saturated at 65504 (round-toward-zero never
+// overflows to infinity).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16),
+                                                                   __uint_as_float(w[i] & 0xFFFF0000u)));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
 
 // 1.0 in all eight bf16 lanes (the "ones" operand whose product gives row sums)
 __device__ __forceinline__ bf16x8_t bf16x8_ones() {
