@@ -80,6 +80,9 @@ constexpr float kLag = 8.0f;      // lag allowed to the running max (log2 units)
 // the first visible score always raises it (anything exceeds it by kLag)
 constexpr float kNoMax = -3.402823466e38f;
 
+// Quotient of non-negative ints (unsigned division: the shorter sequence).
+__device__ __forceinline__ int udiv(int x, int y) { return (int)((unsigned)x / (unsigned)y); }
+
 template <int D>
 struct ChunkCfg {
   static constexpr int KM = D / 32;  // S^T products per block (32 dims each)
@@ -105,13 +108,22 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   // ---- the item: consecutive workgroup indices alternate between the 8
   // XCDs, so each XCD is given a contiguous run of items (the tiles of one
   // (sequence, head) share its L2), heaviest tiles (latest rows) first.
-  const long long items = (long long)a.batch * a.hkv * a.tiles;
-  const long long per = items / 8, rem = items % 8;
-  const int xcd = (int)(blockIdx.x % 8);
-  const long long item = xcd * per + min((long long)xcd, rem) + blockIdx.x / 8;
-  const int bg = (int)(item / a.tiles);
-  const int tile_i = a.tiles - 1 - (int)(item % a.tiles);
-  const int b = bg / a.hkv, g = bg % a.hkv;
+  // (32-bit: the host refuses more than 2^31 - 1 items)
+  const int items = a.batch * a.hkv * a.tiles;
+  const int per = items >> 3, rem = items & 7;
+  const int xcd = (int)(blockIdx.x & 7);
+  const int item = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  const int bg = udiv(item, a.tiles);
+  const int tile_i = a.tiles - 1 - (item - bg * a.tiles);
+  const int b = udiv(bg, a.hkv), g = bg - b * a.hkv;
+  const int *trow = a.table + (size_t)b * a.max_blocks;
+  // the table entries of the wave's first 32 pairs, loaded with the lengths
+  // (bounded by the table row; the visible length masks them below)
+  int tv_first;
+  {
+    const int blk = 2 * (w + kCW * (lane >> 1)) + (lane & 1);
+    tv_first = blk < a.max_blocks ? trow[blk] : -1;
+  }
 
   const int n_ctx = min(max(a.ctx[b], 0), a.max_ctx);
   const int r0 = a.q_start[b], nq = a.q_start[b + 1] - r0;
@@ -264,13 +276,12 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
   // blocks); pair i is staged and computed while pairs i+1 and i+2 are in
   // flight.
   const int npw = npairs > w ? (npairs - w + kCW - 1) / kCW : 0;
-  const int *trow = a.table + (size_t)b * a.max_blocks;
   for (int i0 = 0; i0 < npw; i0 += 32) {
     const int cn = min(32, npw - i0);
     int tv;
     {
       const int blk = 2 * (w + kCW * (i0 + (lane >> 1))) + (lane & 1);
-      tv = blk < nblk ? trow[blk] : -1;
+      tv = blk < nblk ? (i0 == 0 ? tv_first : trow[blk]) : -1;
     }
     auto id_of = [&](int i, int hb) { return __builtin_amdgcn_readlane(tv, 2 * i + hb); };  // i < 32
     auto pair_of = [&](int i) { return w + kCW * (i0 + i); };
@@ -406,13 +417,14 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 
   // ---- the item (same numbering as chunk_kernel: a contiguous run per XCD,
   // latest rows first)
-  const long long items = (long long)a.batch * a.hkv * a.tiles;
-  const long long per = items / 8, rem = items % 8;
-  const int xcd = (int)(blockIdx.x % 8);
-  const long long item = xcd * per + min((long long)xcd, rem) + blockIdx.x / 8;
-  const int bg = (int)(item / a.tiles);
-  const int tile = a.tiles - 1 - (int)(item % a.tiles);
-  const int b = bg / a.hkv, g = bg % a.hkv;
+  // (32-bit: the host refuses more than 2^31 - 1 items)
+  const int items = a.batch * a.hkv * a.tiles;
+  const int per = items >> 3, rem = items & 7;
+  const int xcd = (int)(blockIdx.x & 7);
+  const int item = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  const int bg = udiv(item, a.tiles);
+  const int tile = a.tiles - 1 - (item - bg * a.tiles);
+  const int b = udiv(bg, a.hkv), g = bg - b * a.hkv;
 
   const int n_ctx = min(max(a.ctx[b], 0), a.max_ctx);
   const int r0 = a.q_start[b], nq = a.q_start[b + 1] - r0;
