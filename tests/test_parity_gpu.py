@@ -90,7 +90,11 @@ def test_placed_pools(name):
 def test_head_chunk_from_lengths(case):
     """The kernel takes the host's head chunk when every sequence has the
     block count of max_context_len and the widest one otherwise: both sides
-    of that choice at the Llama-3-8B shape, every sequence against the oracle."""
+    of that choice at the Llama-3-8B shape, every sequence against the oracle.
+    The same cases cover the early first loads: issued and used (a guessed
+    sequence of full length in an equal-length batch), issued and dropped
+    (one_short: the guessed sequence is full but the batch is not), and not
+    issued (ragged lengths)."""
     base = NAMED_SPECS["llama3_8b_b32_ctx4k"]
     rng = np.random.default_rng(3981)
     if case == "equal_blocks":   # 256 blocks each, ragged last blocks
