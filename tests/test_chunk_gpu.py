@@ -280,6 +280,32 @@ def test_chunk_prefill_full_size():
         assert err.max() <= 2e-3
 
 
+def test_chunk_wide_v_at_fp16_range_edge():
+    """The wide kernel over a bf16 pool takes V as fp16.  65280, the largest
+    finite bf16 magnitude not above fp16's 65504, converts exactly: with V
+    entries of +-65280 planted all over the cache, every row stays within the
+    derived bound 2^-10 * sum w|V| + 1e-4.  (The absolute 2e-3 bar means
+    nothing at these magnitudes: fp32 sums alone err by about 65280 * 2^-24.)"""
+    ctx = (300, 700)
+    nq = (300, 129)  # up to 1200 rows per (sequence, KV head) at G = 4: the wide kernel
+    base = make_inputs(_spec("chunk-v-edge", 128, 8, 2, ctx, 1900))
+    v = base.v_pool.copy()
+    rng = np.random.default_rng(1901)
+    idx = rng.integers(0, v.size, size=v.size // 50)
+    v.flat[idx] = np.where(rng.random(idx.size) < 0.5, np.uint16(0x477F), np.uint16(0xC77F))
+    base = dataclasses.replace(base, v_pool=v)
+    ci = chunk_queries(base, nq, 1902)
+    assert rel_of(ci) == REL_F16
+    say(f"[chunk] V at the fp16 range edge, rows={ci.total_rows}")
+    got = gpu_chunk(ci)
+    r = rows_of(ci, range(base.spec.batch))
+    want, bound = oracle_chunk(ci)[r], bound_of(ci)[r]
+    assert np.all(np.isfinite(got[r]))
+    err = np.abs(got[r] - want)
+    assert np.all(err <= bound), f"max excess {(err - bound).max():.3e}"
+    say(f"  max err {err.max():.2e}, max |out| {np.abs(want).max():.3e}")
+
+
 # ---------------------------------------------------------------------------
 # FP8 E4M3 caches (per-token, per-head scales): codes widened to bf16 in the
 # kernels' LDS tiles, the K scale on the score, the V scale on the weight
