@@ -496,9 +496,10 @@ pa_status pa_decode_heads_per_workgroup(const pa_kv_pool *pool, int32_t *heads);
  * pa_profile_enable -- time the attention kernel of the next runs.
  *
  * While enabled (capacity > 0), each run records a pair of HIP events on
- * its stream around its kernel, for up to `capacity` runs; capacity 0
- * disables and releases the events.  Events are host-side HIP objects, not
- * device memory.
+ * its stream, attached to the dispatch of its attention kernel (the start
+ * and the end of the kernel's own execution), for up to `capacity` runs;
+ * capacity 0 disables and releases the events.  Events are host-side HIP
+ * objects, not device memory.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE (capacity < 0), PA_ERR_HIP.
  */
 pa_status pa_profile_enable(pa_kv_pool *pool, int32_t capacity);

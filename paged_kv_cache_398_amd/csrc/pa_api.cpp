@@ -258,15 +258,11 @@ pa_status run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype, int32_t hq, flo
 
   const bool prof = pool->prof_capacity > 0 && pool->prof_count < pool->prof_capacity;
   hipEvent_t *ev = prof ? &pool->prof_events[2 * (size_t)pool->prof_count] : nullptr;
-  if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess)
-    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = pa::launch_attention(a, s)) != hipSuccess)
+  // profiling: the events are attached to the kernel's dispatch, so they
+  // time its own execution (not the queue's markers around it)
+  if ((e = pa::launch_attention(a, s, prof ? ev[0] : nullptr, prof ? ev[1] : nullptr)) != hipSuccess)
     return fail(PA_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
-  if (prof) {
-    if ((e = hipEventRecord(ev[1], s)) != hipSuccess)
-      return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    ++pool->prof_count;
-  }
+  if (prof) ++pool->prof_count;
   return ok();
 }
 
@@ -587,15 +583,10 @@ pa_status pa_decode_kivi_run(pa_kv_pool *pool, const void *q, pa_dtype q_dtype,
   hipError_t e;
   const bool prof = pool->prof_capacity > 0 && pool->prof_count < pool->prof_capacity;
   hipEvent_t *ev = prof ? &pool->prof_events[2 * (size_t)pool->prof_count] : nullptr;
-  if (prof && (e = hipEventRecord(ev[0], s)) != hipSuccess)
-    return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  if ((e = pa::launch_kivi_attention(a, s)) != hipSuccess)
+  if ((e = pa::launch_kivi_attention(a, s, prof ? ev[0] : nullptr, prof ? ev[1] : nullptr)) !=
+      hipSuccess)
     return fail(PA_ERR_HIP, "INT8/INT4 attention kernel launch: %s", hipGetErrorString(e));
-  if (prof) {
-    if ((e = hipEventRecord(ev[1], s)) != hipSuccess)
-      return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-    ++pool->prof_count;
-  }
+  if (prof) ++pool->prof_count;
   return ok();
 }
 

@@ -112,8 +112,11 @@ hipError_t launch_chunk(const ChunkArgs &a, hipStream_t stream);
 // True when a kernel is built for (kv, head_dim, group size).
 bool kernel_supported(int kv, int d, int group);
 
-// Enqueue the attention kernel (grid nwg workgroups of kWaves waves).
-hipError_t launch_attention(const LaunchArgs &a, hipStream_t stream);
+// Enqueue the attention kernel (grid nwg workgroups of kWaves waves).  With
+// ev_start (and ev_stop), the two events record the start and the end of
+// the kernel's own execution (attached to its dispatch).
+hipError_t launch_attention(const LaunchArgs &a, hipStream_t stream,
+                            hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // An INT8 / INT4 pool quantised the KIVI way (codes, fp16 parameters) with
 // the bf16 residual of each sequence's partly filled last block.
@@ -129,7 +132,8 @@ struct KiviArgs {
   int32_t num_blocks, hkv, hq, d, batch, max_blocks, max_ctx, bits;
   float scale_log2e;
 };
-hipError_t launch_kivi_attention(const KiviArgs &a, hipStream_t stream);
+hipError_t launch_kivi_attention(const KiviArgs &a, hipStream_t stream,
+                                 hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_kivi_append(const KiviArgs &a, const void *k_new, const void *v_new,
                               hipStream_t stream);
 

@@ -49,6 +49,8 @@
 #include "pa_internal.h"
 #include "pa_mfma.h"
 
+#include <hip/hip_ext.h>
+
 #include <mutex>
 #include <vector>
 
@@ -1068,27 +1070,31 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t *p, size_t n) {
 }
 
 template <int KV, int D, int G>
-hipError_t launch_attention_t(const LaunchArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((attention_kernel<KV, D, G>), dim3((unsigned)a.nwg), dim3(kThreads), 0, s, a);
+hipError_t launch_attention_t(const LaunchArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0)  // events attached to the dispatch: the kernel's own start and end
+    hipExtLaunchKernelGGL((attention_kernel<KV, D, G>), dim3((unsigned)a.nwg), dim3(kThreads), 0, s,
+                          e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<KV, D, G>), dim3((unsigned)a.nwg), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KV, int D>
-hipError_t by_group(const LaunchArgs &a, hipStream_t s) {
+hipError_t by_group(const LaunchArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.hq / a.hkv) {
-    case 1: return launch_attention_t<KV, D, 1>(a, s);
-    case 2: return launch_attention_t<KV, D, 2>(a, s);
-    case 4: return launch_attention_t<KV, D, 4>(a, s);
-    case 8: return launch_attention_t<KV, D, 8>(a, s);
+    case 1: return launch_attention_t<KV, D, 1>(a, s, e0, e1);
+    case 2: return launch_attention_t<KV, D, 2>(a, s, e0, e1);
+    case 4: return launch_attention_t<KV, D, 4>(a, s, e0, e1);
+    case 8: return launch_attention_t<KV, D, 8>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int KV>
-hipError_t by_dim(const LaunchArgs &a, hipStream_t s) {
+hipError_t by_dim(const LaunchArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.d) {
-    case 64: return by_group<KV, 64>(a, s);
-    case 128: return by_group<KV, 128>(a, s);
+    case 64: return by_group<KV, 64>(a, s, e0, e1);
+    case 128: return by_group<KV, 128>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1100,12 +1106,12 @@ bool kernel_supported(int kv, int d, int group) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t launch_attention(const LaunchArgs &a, hipStream_t s) {
+hipError_t launch_attention(const LaunchArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.batch == 0 || a.nwg == 0) return hipSuccess;
   switch (a.kv) {
-    case KV_F32: return by_dim<KV_F32>(a, s);
-    case KV_BF16: return by_dim<KV_BF16>(a, s);
-    case KV_FP8: return by_dim<KV_FP8>(a, s);
+    case KV_F32: return by_dim<KV_F32>(a, s, e0, e1);
+    case KV_BF16: return by_dim<KV_BF16>(a, s, e0, e1);
+    case KV_FP8: return by_dim<KV_FP8>(a, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

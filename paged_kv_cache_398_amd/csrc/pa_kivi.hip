@@ -52,6 +52,8 @@
 #include "pa_internal.h"
 #include "pa_mfma.h"
 
+#include <hip/hip_ext.h>
+
 namespace pa {
 namespace {
 
@@ -698,19 +700,22 @@ __global__ __launch_bounds__(64) void kivi_append_kernel(KiviArgs a, const void 
 }
 
 template <int BITS, int D, int G>
-void launch_attn(const KiviArgs &a, hipStream_t s) {
+void launch_attn(const KiviArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int threads = kivi_waves<D, G>() * 64;
-  hipLaunchKernelGGL((kivi_attention_kernel<BITS, D, G>), dim3((unsigned)((size_t)a.batch * a.hkv)),
-                     dim3(threads), 0, s, a);
+  const dim3 grid((unsigned)((size_t)a.batch * a.hkv));
+  if (e0)  // events attached to the dispatch: the kernel's own start and end
+    hipExtLaunchKernelGGL((kivi_attention_kernel<BITS, D, G>), grid, dim3(threads), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((kivi_attention_kernel<BITS, D, G>), grid, dim3(threads), 0, s, a);
 }
 
 template <int BITS, int D>
-hipError_t attn_by_group(const KiviArgs &a, hipStream_t s) {
+hipError_t attn_by_group(const KiviArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.hq / a.hkv) {
-    case 1: launch_attn<BITS, D, 1>(a, s); break;
-    case 2: launch_attn<BITS, D, 2>(a, s); break;
-    case 4: launch_attn<BITS, D, 4>(a, s); break;
-    case 8: launch_attn<BITS, D, 8>(a, s); break;
+    case 1: launch_attn<BITS, D, 1>(a, s, e0, e1); break;
+    case 2: launch_attn<BITS, D, 2>(a, s, e0, e1); break;
+    case 4: launch_attn<BITS, D, 4>(a, s, e0, e1); break;
+    case 8: launch_attn<BITS, D, 8>(a, s, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -718,10 +723,11 @@ hipError_t attn_by_group(const KiviArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_kivi_attention(const KiviArgs &a, hipStream_t s) {
+hipError_t launch_kivi_attention(const KiviArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (a.batch == 0) return hipSuccess;
-  if (a.bits == 8) return a.d == 64 ? attn_by_group<8, 64>(a, s) : attn_by_group<8, 128>(a, s);
-  return a.d == 64 ? attn_by_group<4, 64>(a, s) : attn_by_group<4, 128>(a, s);
+  if (a.bits == 8)
+    return a.d == 64 ? attn_by_group<8, 64>(a, s, e0, e1) : attn_by_group<8, 128>(a, s, e0, e1);
+  return a.d == 64 ? attn_by_group<4, 64>(a, s, e0, e1) : attn_by_group<4, 128>(a, s, e0, e1);
 }
 
 hipError_t launch_kivi_append(const KiviArgs &a, const void *k_new, const void *v_new,
