@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention KV-read TB/s, % of 8 TB/s HBM peak; µs per decode step"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_398_amd", "csrc", f)
-               for f in ("pa_kernels.hip", "pa_internal.h")]
+               for f in ("pa_kernels.hip", "pa_internal.h", "pa_mfma.h")]
 
 
 def traffic_file(workload):
@@ -46,7 +46,7 @@ def log(msg):
 
 
 def kernel_source_sha():
-    """Hash of the attention kernel's sources (kernel file and the header it includes)."""
+    """Hash of the attention kernel's sources (kernel file and the headers it includes)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path, "rb") as f:
