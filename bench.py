@@ -299,16 +299,18 @@ def chunk_leg(name, iters, main_inp, main_pools):
         "rows_per_workgroup": rows, "workgroups": s.batch * s.num_kv_heads * per_head,
         "pools_cycled": len(pools),
     }
+    # 256-row workgroups are the wide kernel's (long chunks)
+    kname = "chunk_wide_kernel" if rows >= 256 else "chunk_kernel"
     if hbm_bound:
         a = nbytes / (us * 1e-6) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4),
-                           "kernel": "chunk_kernel"}
+                           "kernel": kname}
     else:
         a = flops / (us * 1e-6) / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": round(a, 1),
                            "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                           "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "kernel": "chunk_kernel"}
+                           "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "kernel": kname}
     log(f"chunk {name}: {us:.1f} us, {res['roofline']['achieved']} "
         f"{res['roofline']['unit']} ({100 * res['roofline']['frac']:.1f}% of peak)")
     return res

@@ -23,7 +23,8 @@
 //  - chunk_wide_kernel, 256 rows per item (long prefill chunks): eight
 //    waves each own 32 rows for the whole visible context, and every 64
 //    tokens are staged once per workgroup in LDS, from where all of them
-//    read their operands.
+//    read their operands; each wave overlaps a pair's softmax with the
+//    products of the pairs before and after it.
 //
 // In both, the products run on the matrix cores (v_mfma_f32_16x16x32_bf16,
 // and _f16 for the wide kernel's PV products over bf16 pools), laid out so
@@ -82,6 +83,44 @@ constexpr float kNoMax = -3.402823466e38f;
 
 // Quotient of non-negative ints (unsigned division: the shorter sequence).
 __device__ __forceinline__ int udiv(int x, int y) { return (int)((unsigned)x / (unsigned)y); }
+
+// A pointer the caller knows to be the same in every lane of the wave, made
+// a scalar value.
+__device__ __forceinline__ const char *wave_ptr(const char *p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+}
+
+// Maxima that return NaN when an operand is NaN (v_maximum3_f32): no
+// quieting of the operands first, unlike fmaxf.  Scores here are finite or
+// -inf.
+__device__ __forceinline__ float max3e(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// the maximum over the four lanes q = 0..3 of a 16-lane column c
+__device__ __forceinline__ float max4q_e(float x) {
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
+}
+
+// Workgroup barrier that publishes LDS writes only.  __syncthreads() also
+// waits for every global load the wave has in flight (its release fence
+// waits for all vector memory operations), which would stall the loads of a
+// later stage issued just before it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <int D>
 struct ChunkCfg {
@@ -360,15 +399,17 @@ __global__ __launch_bounds__(kCThreads) void chunk_kernel(ChunkArgs a) {
 // Long chunks.  One workgroup per kWideRows query rows of a (sequence, KV
 // head); each of its eight waves owns 32 of them (two 16-row tiles) over the
 // whole visible context, so no combine across waves is needed.  Every
-// 64 tokens (four blocks) are staged once per workgroup in LDS (two stages,
-// one barrier per stage; the next stage's global loads are in flight while
-// the current one is computed, as two 32-token pairs) and the waves read
-// their MFMA operands from
-// there: a K/V byte brought to the CU serves 256 rows, a byte read from LDS
-// serves the wave's 32.  Two waves per SIMD let one wave's softmax (VALU)
-// run beside the other's products (MFMA); with four waves of 64 rows, one
-// per SIMD, the two mostly took turns.  The products, masks and online
-// softmax per 16-row tile are those of chunk_kernel.
+// 64 tokens (four blocks) are staged once per workgroup in LDS, in a ring
+// of four stage buffers with one barrier per stage (a stage's global loads
+// are in flight for two pairs' work before they are stored), and the waves
+// read their MFMA operands from there: a K/V byte brought to the CU serves
+// 256 rows, a byte read from LDS serves the wave's 32.  Each wave runs its
+// 32-token pairs as a software pipeline, one step per pair: the PV products
+// of the pair before and the score products of the pair after are issued
+// around the current pair's softmax, and the K operands are read from LDS
+// a step before their products.  Two waves per SIMD; with four waves of 64
+// rows, one per SIMD, the two mostly took turns.  The products, masks and
+// online softmax per 16-row tile are those of chunk_kernel.
 
 constexpr int kWW = 8;                    // waves per workgroup (two per SIMD)
 constexpr int kWT = 16 / kWW;             // 16-row tiles per wave
@@ -376,6 +417,8 @@ constexpr int kWThreads = kWW * 64;
 constexpr int kWideRows = kWW * kWT * 16; // rows per workgroup
 constexpr int kSB = 4;                    // blocks per LDS stage (two pairs)
 constexpr int kSR = kSB * 16;             // token rows per stage
+static_assert(kSR == 64, "FP8 scales: one wave per stage's K or V scales");
+constexpr int kRing = 4;                  // LDS stage buffers in the wide kernel
 
 template <int KV, int D>
 struct WideCfg {
@@ -403,13 +446,14 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   using WC = WideCfg<KV, D>;
   constexpr int KM = C::KM, EV = C::EV;
   constexpr int RSK = WC::RSK, RSV = WC::RSV, NCH = WC::NCH, ROWCH = WC::ROWCH;
-  constexpr int kPH = kWT;  // tiles per softmax phase: all of the wave's
-  static_assert(kWT % kPH == 0, "whole phases");
   constexpr bool ALL = WC::ALL;
-  __shared__ __align__(16) char s_kv[2 * WC::STAGE];
+  // how far ahead the K operands are read: two pairs, except over FP8
+  // pools, whose two-term weights leave no room for them in registers
+  constexpr int kKAhead = KV == KV_FP8 ? 1 : 2;
+  __shared__ __align__(16) char s_kv[kRing * WC::STAGE];  // a ring of stages
   __shared__ __align__(16) float s_f[kWW][16];  // per-row rescaling factors
   // FP8: the K and V scales of each stage's tokens (0 for slots not real)
-  __shared__ __align__(16) float s_sc[KV == KV_FP8 ? 2 : 1][2][kSR];
+  __shared__ __align__(16) float s_sc[KV == KV_FP8 ? kRing : 1][2][kSR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,7 +486,13 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   const bool has_rows = wrow0 < nrows;
   const int pfirst = n_ctx - nq + wrow0 / G;                       // first row's position
   const int plast = n_ctx - nq + (min(wrow0 + 16 * kWT, nrows) - 1) / G;  // last row's position
+  const int np = has_rows && plast >= 0 ? plast / 32 + 1 : 0;  // pairs visible to the wave
 
+  // a negative scale is carried by the queries' signs (exact in bf16), so
+  // that the multiplier sl2 of the scores is non-negative
+  const bool neg = a.scale_log2e < 0.f;
+  const float sl2 = neg ? -a.scale_log2e : a.scale_log2e;
+  const uint32_t qflip = neg ? 0x80008000u : 0u;
   bf16x8_t qf[kWT][KM];
   int prow[kWT];
   f32x4_t o[kWT][EV];
@@ -457,7 +507,8 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
                          ((size_t)(r0 + (v ? r / G : 0)) * a.hq + g * G + (v ? r % G : 0)) * D + 8 * q;
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
-      const uint4 x = v ? *reinterpret_cast<const uint4 *>(qp + 32 * m) : make_uint4(0, 0, 0, 0);
+      uint4 x = v ? *reinterpret_cast<const uint4 *>(qp + 32 * m) : make_uint4(0, 0, 0, 0);
+      x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
       qf[t][m] = as_bf16x8(x);
     }
     mrun[t] = kNoMax;
@@ -465,7 +516,6 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 #pragma unroll
     for (int m = 0; m < EV; ++m) o[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const float sl2 = a.scale_log2e;
   const bf16x8_t ones = bf16x8_ones();
   const f16x8_t ones16 = f16x8_ones();
   // the type of the staged V rows and PV operands: fp16 over bf16 pools
@@ -508,7 +558,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   uint4 sk[NCH], sv[NCH];
   bool sreal[NCH];
   bool sall = true;  // every slot of the stage real (wave-uniform)
-  float ssc = 0.f;   // FP8: the scale thread tid < 2 kSR moves (K for tid < kSR, then V)
+  float ssc = 0.f;   // FP8: the scale thread tid < 2 kSR moves (wave 0: K, wave 1: V)
   auto stage_load = [&](int sg) {
     const int blk0 = kSB * sg;
     int id[kSB];
@@ -527,18 +577,25 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
       const bool ok = (unsigned)bid < (unsigned)a.num_blocks;
       sreal[i] = ok && (blk0 + c_hb[i]) * kTok + c_slot[i] < n_ctx;
       const size_t boff = ok ? (size_t)bid * block_bytes : 0;
-      sk[i] = *reinterpret_cast<const uint4 *>(kbase + boff + c_src[i]);
-      sv[i] = *reinterpret_cast<const uint4 *>(vbase + boff + c_src[i]);
+      // the block's base is the same for the whole wave: held in scalar
+      // registers, the load adds the lane's 32-bit offset (no 64-bit
+      // address per lane kept live across the loop)
+      sk[i] = *reinterpret_cast<const uint4 *>(wave_ptr(kbase + boff) + c_src[i]);
+      sv[i] = *reinterpret_cast<const uint4 *>(wave_ptr(vbase + boff) + c_src[i]);
     }
     if constexpr (KV == KV_FP8) {
-      if (tid < 2 * kSR) {
+      if (w < 2) {  // kSR = 64: one wave per scale
         const int r = tid % kSR, hb = r >> 4, slot = r & 15;
         int bid = id[0];
 #pragma unroll
         for (int h = 1; h < kSB; ++h) bid = hb == h ? id[h] : bid;
         const bool ok = (unsigned)bid < (unsigned)a.num_blocks;
-        const float *sc = tid < kSR ? a.k_scale : a.v_scale;
-        const float x = sc[((ok ? (size_t)bid : 0) * a.hkv + g) * kTok + slot];
+        // the table's base for head g in scalar registers, the block and
+        // slot per lane
+        const char *sc = wave_ptr(reinterpret_cast<const char *>(w == 0 ? a.k_scale : a.v_scale) +
+                                  (size_t)g * kTok * sizeof(float));
+        const size_t off = ((ok ? (size_t)bid : 0) * a.hkv * kTok + slot) * sizeof(float);
+        const float x = *reinterpret_cast<const float *>(sc + off);
         ssc = ok && (blk0 + hb) * kTok + slot < n_ctx ? x : 0.f;
       }
     }
@@ -563,10 +620,11 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     else
       put(dst, x);
   };
-  auto stage_store = [&](int st) {
+  auto stage_store = [&](int sg) {
+    const int st = sg & (kRing - 1);  // its buffer in the ring
     char *base = s_kv + st * WC::STAGE;
     if constexpr (KV == KV_FP8) {
-      if (tid < 2 * kSR) s_sc[st][tid / kSR][tid % kSR] = ssc;
+      if (w < 2) s_sc[st][w][lane] = ssc;
     }
     if (sall) {
 #pragma unroll
@@ -587,114 +645,145 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
     }
   };
 
-  // ---- one pair (blocks blk0, blk0 + 1) for the wave's tiles, from its
-  // rows r0s .. r0s + 31 of LDS stage st
-  auto compute = [&](int blk0, int st, int r0s) {
-    bool ok[2];
-    ok[0] = (unsigned)block_id(blk0) < (unsigned)a.num_blocks;
-    ok[1] = (unsigned)block_id(blk0 + 1) < (unsigned)a.num_blocks;
-    const bool full = ok[0] && ok[1] && (blk0 + 2) * kTok - 1 <= pfirst;
-    const char *lk = s_kv + st * WC::STAGE + r0s * RSK;
-    const char *lv = s_kv + st * WC::STAGE + kSR * RSK + r0s * RSV;
-    // FP8: scales of tokens 4q .. 4q+3 of block hb of the pair (read where
-    // used, which keeps the kernel within its 256 registers)
-    auto scales = [&](int which, int hb) {
-      return *reinterpret_cast<const float4 *>(&s_sc[KV == KV_FP8 ? st : 0][which][r0s + 16 * hb + 4 * q]);
-    };
-    // A operands of S^T: token c of block hb, dims 32m + 8q .. +7
-    uint4 kop[2][KM];
+  // ---- the software pipeline.  Pair j of the wave (blocks 2j, 2j + 1, in
+  // LDS stage j / 2, token rows 32 (j % 2) .. +31) goes through three steps:
+  // its score products are issued at the end of step j - 1, its softmax
+  // runs in step j and its PV products are issued in step j + 1.  So step j
+  // holds
+  //   the rescaling of O and l for a rise of the running max in step j - 1;
+  //   the PV products of pair j - 1, next to the maxima of pair j;
+  //   pair j's exponentials (while those products run);
+  //   the score products of pair j + 1 (while the next step starts).
+  // Step j reads the stages of pairs j - 1, j and j + 1, up to three of
+  // them: the stages live in a ring of three LDS buffers.  The stage after
+  // next is stored between the two steps of a stage and published by the
+  // barrier right after, which orders every wave's reads of the buffer it
+  // overwrites (its stage is two behind) before the store.
+  auto stage_of = [&](int p) { return (p >> 1) & (kRing - 1); };  // LDS buffer of pair p's stage
+  // FP8: scales of tokens 4q .. 4q+3 of block hb of pair p (read where used,
+  // which keeps the kernel within its 256 registers)
+  auto scales = [&](int which, int p, int hb) {
+    return *reinterpret_cast<const float4 *>(
+        &s_sc[KV == KV_FP8 ? stage_of(p) : 0][which][32 * (p & 1) + 16 * hb + 4 * q]);
+  };
+  // per-lane byte offsets in a stage: the K operand (token c, dims 8q ..
+  // 8q + 7) and the transposing V read (token 4q + c / 4, dims 4 (c % 4) ..)
+  const uint32_t lane_k = c * RSK + 16 * q;
+  const uint32_t lane_v = kSR * RSK + (4 * q + (c >> 2)) * RSV + 8 * (c & 3);
+  // the A operands of pair p's score products: token c of block hb, dims
+  // 32m + 8q .. +7
+  auto kload = [&](int p, uint4 (&kop)[2][KM]) {
+    const char *lk = s_kv + stage_of(p) * WC::STAGE + 32 * (p & 1) * RSK + lane_k;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int m = 0; m < KM; ++m)
-        kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + (16 * hb + c) * RSK + (32 * m + 8 * q) * 2);
-    // the tiles in groups of kPH: all score products of a group first, then
-    // the softmax of all its tiles with one (rarely taken) rescaling branch,
-    // then all PV products -- a single basic block in the common case, so
-    // the scheduler can overlap one tile's VALU work with another's MFMAs
+        kop[hb][m] = *reinterpret_cast<const uint4 *>(lk + 16 * hb * RSK + 64 * m);
+  };
+  // the score products of a pair from its A operands
+  auto score = [&](const uint4 (&kop)[2][KM], f32x4_t (&s)[kWT][2]) {
 #pragma unroll
-    for (int t0 = 0; t0 < kWT; t0 += kPH) {
-      float x[kPH][2][4];
-      float mx[kPH];
+    for (int u = 0; u < kWT; ++u)
 #pragma unroll
-      for (int u = 0; u < kPH; ++u) {
-        f32x4_t s[2];
+      for (int hb = 0; hb < 2; ++hb) {
+        s[u][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          s[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < KM; ++m)
-            s[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[t0 + u][m], s[hb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          float ksc[4] = {1.f, 1.f, 1.f, 1.f};
-          if constexpr (KV == KV_FP8) {
-            const float4 k4 = scales(0, hb);
-            ksc[0] = k4.x; ksc[1] = k4.y; ksc[2] = k4.z; ksc[3] = k4.w;
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[u][hb][j] = s[hb][j] * sl2;
-            if constexpr (KV == KV_FP8) x[u][hb][j] *= ksc[j];
-          }
-        }
-        mx[u] = max8(x[u]);
+        for (int m = 0; m < KM; ++m)
+          s[u][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop[hb][m]), qf[u][m], s[u][hb], 0, 0, 0);
       }
-      if (!full) {
+  };
+  // the weights a pair's softmax leaves for its PV products one step later:
+  // fp16 over bf16 pools; over FP8 pools hi + lo bf16, for the row sums and
+  // (with the V scale) for the products
+  f16x8_t pw16[kWT];
+  bf16x8_t pwb[KV == KV_FP8 ? kWT : 1][4];
+  f32x4_t sc[kWT][2];  // the scores of the pair whose softmax runs next
+  // K operands read ahead: those of pair j + 1 during step j when kKAhead
+  // is 2 (read at the end of step j - 1), else read where used
+  uint4 kpre[2][KM];
+  // a rise of the running max in the last step, with the maxima before it
+  bool pend = false;
+  float mold[kWT];
+  (void)pw16;
+  (void)pwb;
+
+  // step j.  hp: the PV products of pair j - 1 are due; hc: pair j has
+  // scores, in sc; hn: pair j + 1 exists, its scores go to sn
+  auto step = [&](int j, auto HP, auto HC, auto HN) {
+    constexpr bool hp = decltype(HP)::value, hc = decltype(HC)::value, hn = decltype(HN)::value;
+    // the rescaling due from the previous step's rise of the running max
+    // (rows not raised: exp2(0) = 1)
+    if (pend) {
 #pragma unroll
-        for (int u = 0; u < kPH; ++u) {
+      for (int u = 0; u < kWT; ++u) {
+        const float f = __builtin_amdgcn_exp2f(mold[u] - mrun[u]);
+        // lane (c, q) holds the factor of row c; its O and l entries are
+        // rows 4q .. 4q+3: fetch those rows' factors from lanes 4q + r
+        // through LDS: row c's lanes write it, then every lane reads its
+        // four rows' factors at once
+        if (q == 0) s_f[w][c] = f;
+        __builtin_amdgcn_wave_barrier();
+        const float4 f4 = *reinterpret_cast<const float4 *>(&s_f[w][4 * q]);
+        __builtin_amdgcn_wave_barrier();
+        const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          l4[u][r] *= fr[r];
+#pragma unroll
+          for (int m = 0; m < EV; ++m) o[u][m][r] *= fr[r];
+        }
+      }
+      pend = false;
+    }
+    // pair j's maxima: over the raw scores when the pair needs no mask
+    // (the multiplier is non-negative, so it scales the maximum too);
+    // otherwise over the scaled, masked scores, which replace the raw ones
+    float mloc[kWT];
+    float kx = 1.f;  // multiplier of sc in the exponent (wave-uniform)
+    if constexpr (hc) {
+      const int blk0 = 2 * j;
+      const bool ok0 = (unsigned)block_id(blk0) < (unsigned)a.num_blocks;
+      const bool ok1 = (unsigned)block_id(blk0 + 1) < (unsigned)a.num_blocks;
+      const bool full = ok0 && ok1 && (blk0 + 2) * kTok - 1 <= pfirst;
+      if (KV == KV_BF16 && full) {
+        kx = sl2;
+      } else {
+#pragma unroll
+        for (int u = 0; u < kWT; ++u)
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
+            float ksc[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (KV == KV_FP8) {
+              const float4 k4 = scales(0, j, hb);
+              ksc[0] = k4.x; ksc[1] = k4.y; ksc[2] = k4.z; ksc[3] = k4.w;
+            }
+            const bool okh = hb ? ok1 : ok0;
             const int tok0 = (blk0 + hb) * kTok + 4 * q;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              x[u][hb][j] = (ok[hb] && tok0 + j <= prow[t0 + u]) ? x[u][hb][j] : -__builtin_huge_valf();
+            for (int e = 0; e < 4; ++e) {
+              float x = sc[u][hb][e] * sl2;
+              if constexpr (KV == KV_FP8) x *= ksc[e];
+              sc[u][hb][e] = full || (okh && tok0 + e <= prow[u]) ? x : -__builtin_huge_valf();
+            }
           }
-          mx[u] = max8(x[u]);
-        }
       }
-      bool raise[kPH];
-      bool any = false;
 #pragma unroll
-      for (int u = 0; u < kPH; ++u) {
-        mx[u] = max4q(mx[u]);
-        raise[u] = mx[u] > mrun[t0 + u] + kLag;
-        any = any || raise[u];
-      }
-      if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-        for (int u = 0; u < kPH; ++u) {
-          const int t = t0 + u;
-          const float mn = raise[u] ? mx[u] : mrun[t];
-          const float f = raise[u] ? __builtin_amdgcn_exp2f(mrun[t] - mn) : 1.f;
-          mrun[t] = mn;
-          // lane (c, q) holds the factor of row c; its O and l entries are
-          // rows 4q .. 4q+3: fetch those rows' factors from lanes 4q + r
-          // through LDS: row c's lanes write it, then every lane reads its
-          // four rows' factors at once (cross-lane permutes per row kept
-          // more registers live and made the kernel spill)
-          if (q == 0) s_f[w][c] = f;
-          __builtin_amdgcn_wave_barrier();
-          const float4 f4 = *reinterpret_cast<const float4 *>(&s_f[w][4 * q]);
-          __builtin_amdgcn_wave_barrier();
-          const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            l4[t][r] *= fr[r];
-#pragma unroll
-            for (int m = 0; m < EV; ++m) o[t][m][r] *= fr[r];
-          }
-        }
-      }
-      // B operands of O = P V, one per 16 dims (slab m): lane (n = c, q)
-      // needs V[token 4q + e of block hb][dim 16m + n] for e = 0..3, hb = 0, 1.
-      // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of
-      // the 8 bytes addressed by lanes 4r + i / 4, r = 0..3 (checked on the
-      // GPU with a one-wave probe); so lane 4r + s addresses token 4q + r,
-      // dims 16m + 4s .. 16m + 4s + 3, of the row-major V rows in LDS.
-      // (read after the score products, so that these registers and the K
-      // operands' are not live at once)
+      for (int u = 0; u < kWT; ++u)
+        mloc[u] = max3e(max3e(sc[u][0][0], sc[u][0][1], sc[u][0][2]), max3e(sc[u][0][3], sc[u][1][0], sc[u][1][1]),
+                        max3e(sc[u][1][2], sc[u][1][3], sc[u][1][3]));
+    }
+
+    // A. PV products of pair j - 1.  B operands, one per 16 dims (slab m):
+    // lane (n = c, q) needs V[token 4q + e of block hb][dim 16m + n] for
+    // e = 0..3, hb = 0, 1.  ds_read_b64_tr_b16 gives lane i of a 16-lane
+    // group element i % 4 of the 8 bytes addressed by lanes 4r + i / 4,
+    // r = 0..3 (checked on the GPU with a one-wave probe); so lane 4r + s
+    // addresses token 4q + r, dims 16m + 4s .. 16m + 4s + 3, of the
+    // row-major V rows in LDS.  Lane (c, q)'s eight weights are row c's
+    // tokens 4q .. 4q+3 of both blocks, the same k order.
+    if constexpr (hp) {
+      const int p = j - 1;
+      const char *lv = s_kv + stage_of(p) * WC::STAGE + 32 * (p & 1) * RSV + lane_v;
       VOp vb[EV];
 #pragma unroll
       for (int m = 0; m < EV; ++m) {
@@ -702,77 +791,132 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
           h[hb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s_t *)(lv + (16 * hb + 4 * q + (c >> 2)) * RSV + (16 * m + 4 * (c & 3)) * 2));
+              (lds_v4s_t *)(lv + 16 * hb * RSV + 32 * m));
         vb[m] = __builtin_bit_cast(VOp, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
-      for (int u = 0; u < kPH; ++u) {
-        const int t = t0 + u;
-        const float nm = -mrun[t];
+      for (int u = 0; u < kWT; ++u) {
+        if constexpr (KV == KV_BF16) {
+          // fp16 weights (within a relative 2^-11) and fp16 V, one product
+          // per slab; the row sums from the same fp16 weights
+          l4[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw16[u], ones16, l4[u], 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < EV; ++m)
+            o[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw16[u], vb[m], o[u][m], 0, 0, 0);
+        } else {
+          // FP8: the weights as hi + lo bf16, two products per slab
+          l4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pwb[u][0], ones, l4[u], 0, 0, 0);
+          l4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pwb[u][1], ones, l4[u], 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < EV; ++m) {
+            o[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pwb[u][2], vb[m], o[u][m], 0, 0, 0);
+            o[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pwb[u][3], vb[m], o[u][m], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // the lagged running max: raised only when a pair's max exceeds it by
+    // more than kLag.  O and l are rescaled at the start of the next step:
+    // after pair j - 1's products (issued above), before pair j's.
+    if constexpr (hc) {
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < kWT; ++u) {
+        const float mx = max4q_e(mloc[u]) * kx;
+        const bool raise = mx > mrun[u] + kLag;
+        any = any || raise;
+        mold[u] = mrun[u];
+        mrun[u] = raise ? mx : mrun[u];
+      }
+      pend = __builtin_amdgcn_ballot_w64(any) != 0;
+    }
+
+    // B. score products of pair j + 1; pair j's weights
+    if constexpr (hc) {
+#pragma unroll
+      for (int u = 0; u < kWT; ++u) {
+        const float nm = -mrun[u];
         float pf[8];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pf[4 * hb + j] = __builtin_amdgcn_exp2f(x[u][hb][j] + nm);
-        // O = P V: lane (c, q)'s eight weights are row c's tokens 4q .. 4q+3
-        // of both blocks, the same k order as vb
+          for (int e = 0; e < 4; ++e) pf[4 * hb + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][hb][e], kx, nm));
         if constexpr (KV == KV_BF16) {
-          // bf16 pools: fp16 weights (within a relative 2^-11) and fp16 V,
-          // one product per slab; the row sums from the same fp16 weights
-          const f16x8_t p16 = to_f16x8(pf);
-          l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, ones16, l4[t], 0, 0, 0);
-#pragma unroll
-          for (int m = 0; m < EV; ++m)
-            o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p16, vb[m], o[t][m], 0, 0, 0);
-          continue;
-        }
-        // FP8 pools: the weights as hi + lo bf16, two products per slab
-        bf16x8_t ph, pl;
-        split_bf16(pf, ph, pl);
-        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, ones, l4[t], 0, 0, 0);
-        l4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, ones, l4[t], 0, 0, 0);
-        bf16x8_t wh = ph, wl = pl;
-        if constexpr (KV == KV_FP8) {  // the V scale multiplies the PV weight
+          pw16[u] = to_f16x8(pf);
+        } else {
+          // the V scale multiplies the PV weight (masked: 0 x 0)
+          split_bf16(pf, pwb[u][0], pwb[u][1]);
           float pv[8];
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
-            const float4 v4 = scales(1, hb);
+            const float4 v4 = scales(1, j, hb);
             const float vsc[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pv[4 * hb + j] = pf[4 * hb + j] * vsc[j];  // masked: 0 x 0
+            for (int e = 0; e < 4; ++e) pv[4 * hb + e] = pf[4 * hb + e] * vsc[e];
           }
-          split_bf16(pv, wh, wl);
+          split_bf16(pv, pwb[u][2], pwb[u][3]);
         }
-#pragma unroll
-        for (int m = 0; m < EV; ++m) {
-          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, vb[m], o[t][m], 0, 0, 0);
-          o[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, vb[m], o[t][m], 0, 0, 0);
-        }
+      }
+    }
+    // the score products of pair j + 1, into the registers pair j's
+    // exponentials have just read; then the K operands of pair j + 2
+    if constexpr (hn) {
+      if constexpr (kKAhead == 2) {
+        score(kpre, sc);
+        kload(j + 2, kpre);
+      } else {
+        kload(j + 1, kpre);
+        score(kpre, sc);
       }
     }
   };
+  // the parts of a step are fixed at compile time (branches on them would
+  // make the accumulators go through copies).  Every step of the loop is
+  // the steady form: step np, one past the wave's last visible pair, takes
+  // the pair after it as fully masked (its positions are past every row's,
+  // so its weights are exactly 0 and the running max stays), and issues
+  // score products for the pair after that, never used; later steps are
+  // skipped.  Their K reads stay inside the ring of LDS buffers.
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // before step j = 2t (even), stage t + 1 is stored and published (step
+  // j reads the K operands of its first pair) and stage t + 2 loaded
+  auto handoff = [&](int j) {
+    const int t = j >> 1;
+    if (t + 1 < nstages) {
+      stage_store(t + 1);
+      if (t + 2 < nstages) stage_load(t + 2);
+    }
+    lds_barrier();
+  };
 
-  // ---- main loop: every wave takes part in the staging and the barriers,
-  // also when none of a stage's tokens is visible to its rows
+  // ---- main loop, one step per pair; every wave takes part in the staging
+  // and the barriers to the end, also after its last visible pair
   if (nstages > 0) {
     stage_load(0);
     stage_store(0);
-    __syncthreads();
-    for (int sg = 0; sg < nstages; ++sg) {
-      const int st = sg & 1;
-      const bool more = sg + 1 < nstages;
-      if (more) stage_load(sg + 1);
-#pragma unroll
-      for (int sp = 0; sp < kSB / 2; ++sp) {
-        const int blk0 = kSB * sg + 2 * sp;
-        // nothing of the pair (or of the ones after it) visible to the wave
-        if (!has_rows || blk0 * kTok > plast) break;
-        compute(blk0, st, 32 * sp);
-      }
-      // stage st ^ 1 was last read in the previous pass, before its barrier
-      if (more) stage_store(st ^ 1);
-      __syncthreads();
+    if (nstages > 1) stage_load(1);
+    lds_barrier();
+    handoff(0);  // stage 1
+    if (np > 0) {
+      kload(0, kpre);
+      score(kpre, sc);
+      if constexpr (kKAhead == 2) kload(1, kpre);
+      step(0, F_{}, T_{}, T_{});
     }
+    // the wave's steps (none behind a branch, so that the accumulators stay
+    // in place), then the staging of the rest
+    const int jl = min(np, 2 * nstages - 1);
+    int j = 1;
+    for (; j <= jl; ++j) {
+      if (!(j & 1)) handoff(j);
+      step(j, T_{}, T_{}, T_{});
+    }
+    for (; j < 2 * nstages; ++j)
+      if (!(j & 1)) handoff(j);
+    // the last pair's PV products, when the wave sees every pair
+    if (np == 2 * nstages) step(np, T_{}, F_{}, F_{});
   }
 
   // ---- normalise and write the wave's rows: lane (n = c, q) holds dim
