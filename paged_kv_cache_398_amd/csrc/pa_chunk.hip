@@ -653,12 +653,14 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   //   the rescaling of O and l for a rise of the running max in step j - 1;
   //   the PV products of pair j - 1, next to the maxima of pair j;
   //   pair j's exponentials (while those products run);
-  //   the score products of pair j + 1 (while the next step starts).
-  // Step j reads the stages of pairs j - 1, j and j + 1, up to three of
-  // them: the stages live in a ring of three LDS buffers.  The stage after
-  // next is stored between the two steps of a stage and published by the
-  // barrier right after, which orders every wave's reads of the buffer it
-  // overwrites (its stage is two behind) before the store.
+  //   the score products of pair j + 1 (while the next step starts), and
+  //   over bf16 pools the K operands of pair j + 2.
+  // Step j reads the stages of pairs j - 1 to j + 2: the stages live in a
+  // ring of kRing = 4 LDS buffers.  Stage t + 1 is stored before step 2t and
+  // published by the barrier right after; it overwrites stage t - 3, whose
+  // last read (the V operands of pair 2t - 5, in step 2t - 4) every wave
+  // has made before the barrier of the previous stage, which the storing
+  // wave has passed.
   auto stage_of = [&](int p) { return (p >> 1) & (kRing - 1); };  // LDS buffer of pair p's stage
   // FP8: scales of tokens 4q .. 4q+3 of block hb of pair p (read where used,
   // which keeps the kernel within its 256 registers)
