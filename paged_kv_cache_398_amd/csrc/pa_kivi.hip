@@ -43,9 +43,10 @@
 // pattern of 128 gives 128 + code, two channels per instruction, in the
 // order (0,4), (1,5), (2,6), (3,7) of each 8 (the q s pieces follow that
 // order, the output dims are permuted back at the end).  The 128 so added
-// is removed exactly, from the same bf16 terms, on the matrix cores: for K
-// by products of the pieces with a -128 operand, for V by the sum of the
-// weights (a product with a ones operand) times 128.
+// is removed from the same bf16 terms: for K, 128 times the sum of each
+// row's pieces is subtracted from the row's per-block constant (v_dot2
+// against -128, two terms per instruction, when the pieces are made); for
+// V, the sum of the weights (a product with a ones operand) times 128.
 // The waves' exact states (running max, sum, unnormalised output) are
 // combined in LDS.
 
@@ -201,8 +202,11 @@ struct QPair {
   int lim[2];             // valid tokens of each block: 16 or 0 (a residual: 0 .. 15)
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 template <int BITS, int D, int G>
 __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kernel(KiviArgs a) {
+  constexpr bool kBiased = BITS == 4;  // K codes widened to 128 + code
   constexpr int kKW = kivi_waves<D, G>();
   using Q = QGeo<BITS, D, G>;
   constexpr int KM = Q::KM, EV = Q::EV, RSV = Q::RSV, FPL = Q::FPL, NFR = Q::NFR;
@@ -285,7 +289,7 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
   // The q s pieces of block hb of the pair (fp16 scales s, mins m) into LDS,
   // and the block's per-row constant sum_c q m_c.  INT4 pieces are in the
   // channel order of the widened INT4 codes.
-  auto pieces = [&](int hb, const uint4 (&s)[FPL], const uint4 (&m)[FPL]) {
+  auto pieces = [&](int hb, const uint4 (&s)[FPL], const uint4 (&m)[FPL], bool bias) {
     char *fr = s_frag[w][hb];
     float cst_all = 0.f;
 #pragma unroll
@@ -305,6 +309,19 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
       for (int e = 0; e < 8; ++e) p[e] = BITS == 8 ? qs[e] : qs[(e >> 1) + 4 * (e & 1)];
       bf16x8_t hi, lo;
       split_bf16(p, hi, lo);
+      if (bias) {
+        // the widened INT4 K codes carry 128 + code: their products with
+        // these pieces hold 128 sum(hi + lo), removed here from the row's
+        // constant with the same bf16 terms (two per dot product)
+        const bf16x2_t n128 = __builtin_bit_cast(bf16x2_t, 0xC300C300u);
+        const uint4 h4 = __builtin_bit_cast(uint4, hi), l4 = __builtin_bit_cast(uint4, lo);
+        const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w}, lw[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          cst = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hw[e]), n128, cst, false);
+          cst = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lw[e]), n128, cst, false);
+        }
+      }
       if (lane + 64 * i < NFR) {
         *reinterpret_cast<bf16x8_t *>(fr + (lane + 64 * i) * 16) = hi;
         *reinterpret_cast<bf16x8_t *>(fr + KM * G * 64 + (lane + 64 * i) * 16) = lo;
@@ -340,8 +357,8 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
 
   auto stage = [&](const QLoads<BITS, D, G> &L) {
     stage_v(L);
-    pieces(0, L.ks[0], L.km[0]);
-    pieces(1, L.ks[1], L.km[1]);
+    pieces(0, L.ks[0], L.km[0], kBiased);
+    pieces(1, L.ks[1], L.km[1], kBiased);
     QPair<BITS, D, G> P;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -365,9 +382,6 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
 #pragma unroll
   for (int m = 0; m < EV; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bf16x8_t ones = bf16x8_ones();
-  // -128 in all eight lanes: its products with the q s pieces remove the 128
-  // that the widened INT4 K codes carry
-  const bf16x8_t neg128 = as_bf16x8(make_uint4(0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u));
 
   auto compute = [&](const QPair<BITS, D, G> &P, bool biased) {
     __builtin_amdgcn_wave_barrier();  // tile and pieces were written by other lanes
@@ -384,10 +398,6 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
         const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(fr + (KM + m) * G * 64);
         sc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P.ka[hb][m], bh, sc[hb], 0, 0, 0);
         sc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(P.ka[hb][m], bl, sc[hb], 0, 0, 0);
-        if (biased) {
-          sc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, bh, sc[hb], 0, 0, 0);
-          sc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg128, bl, sc[hb], 0, 0, 0);
-        }
       }
       cst[hb] = s_cst[w][hb][cs];
     }
@@ -468,7 +478,6 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
   // staged and computed while pairs p + 1 and p + 2 load).  The table
   // entries of up to 64 blocks come from one vector load (lane j holds the
   // wave's block c0 + j; -1 past the wave's blocks), read with readlane.
-  constexpr bool kBiased = BITS == 4;
   const int nbw = nf > w ? (nf - w + kKW - 1) / kKW : 0;
   const int *trow = a.table + (size_t)b * a.max_blocks;
   for (int c0 = 0; c0 < nbw; c0 += 64) {
@@ -538,7 +547,7 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
       s1[i] = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // fp16 1.0
       m0[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    pieces(0, s1, m0);
+    pieces(0, s1, m0, false);
     P.vp[0] = P.vp[1] = make_uint4(0x3C00u, 0x3C00u, 0x3C00u, 0x3C00u);  // (scale 1, min 0)
     P.lim[0] = nres;
     P.lim[1] = 0;
