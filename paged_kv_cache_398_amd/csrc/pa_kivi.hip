@@ -298,9 +298,11 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
       const uint32_t mw[4] = {m[i].x, m[i].y, m[i].z, m[i].w};
       float qs[8], cst = 0.f;
 #pragma unroll
+      // (products written as fma with 0: one v_fma_mix_f32 each, taking
+      // the fp16 operand as it is, instead of a conversion and a multiply)
       for (int e = 0; e < 4; ++e) {
-        qs[2 * e] = qf[i][2 * e] * half_lo(sw[e]);
-        qs[2 * e + 1] = qf[i][2 * e + 1] * half_hi(sw[e]);
+        qs[2 * e] = fmaf(qf[i][2 * e], half_lo(sw[e]), 0.f);
+        qs[2 * e + 1] = fmaf(qf[i][2 * e + 1], half_hi(sw[e]), 0.f);
         cst = fmaf(qf[i][2 * e], half_lo(mw[e]), cst);
         cst = fmaf(qf[i][2 * e + 1], half_hi(mw[e]), cst);
       }
@@ -447,7 +449,7 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t vp = vpa[e];
-        wv[e] = pf[e] * half_lo(vp);
+        wv[e] = fmaf(pf[e], half_lo(vp), 0.f);
         psum = fmaf(pf[e], half_hi(vp), psum);
       }
     } else {
@@ -456,7 +458,7 @@ __global__ __launch_bounds__((kivi_waves<D, G>() * 64)) void kivi_attention_kern
         const uint32_t vp = vpa[e];
         // a dead slot's parameters may be anything (NaN included): weight 0
         const bool live = 4 * q + (e & 3) < P.lim[e >> 2];
-        wv[e] = live ? pf[e] * half_lo(vp) : 0.f;
+        wv[e] = live ? fmaf(pf[e], half_lo(vp), 0.f) : 0.f;
         psum = live ? fmaf(pf[e], half_hi(vp), psum) : psum;
       }
     }
