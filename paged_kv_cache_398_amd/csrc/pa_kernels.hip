@@ -418,6 +418,7 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
     }
   };
 
+  constexpr bool kOneBlock = KV == KV_F32 && G * D >= 1024;
   // ---- main loop: a two-stage pipeline over the wave's blocks, block i+1 in
   // flight while block i is computed.  The table entries of up to 64 blocks
   // are fetched by one vector load (lane j holds block c0 + j) before the
@@ -428,6 +429,15 @@ __device__ __forceinline__ void attend_piece(const LaunchArgs &a, int b, int g, 
     auto entry = [&](int i) { return __builtin_amdgcn_readlane(tv, min(i, cn - 1)); };
     Block<KV, D, G> A, B;
     issue(A, c0, entry(0));
+    if constexpr (kOneBlock) {
+      // fp32 rows with eight query heads: the accumulators and queries
+      // (2 G D / LPT registers) leave no room for a second block in flight
+      for (int i = 0; i < cn; ++i) {
+        if (i > 0) issue(A, c0 + i, entry(i));
+        compute(A);
+      }
+      continue;
+    }
     // The scheduling barriers keep the next block's loads ahead of the
     // first use of the current block; without them the compiler sinks the
     // loads below that use and the two blocks are fetched one after another.
