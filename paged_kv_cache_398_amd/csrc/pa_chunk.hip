@@ -710,7 +710,8 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWW /
   (void)pwb;
 
   // step j.  hp: the PV products of pair j - 1 are due; hc: pair j has
-  // scores, in sc; hn: pair j + 1 exists, its scores go to sn
+  // scores, in sc; hn: pair j + 1's score products are issued (into sc,
+  // after pair j's exponentials have read it)
   auto step = [&](int j, auto HP, auto HC, auto HN) {
     constexpr bool hp = decltype(HP)::value, hc = decltype(HC)::value, hn = decltype(HN)::value;
     // the rescaling due from the previous step's rise of the running max
