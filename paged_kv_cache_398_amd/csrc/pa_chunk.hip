@@ -422,15 +422,14 @@ constexpr int kRing = 4;                  // LDS stage buffers in the wide kerne
 
 template <int KV, int D>
 struct WideCfg {
-  // LDS row strides (bytes), one per region, each making its reads
-  // conflict-free: a K operand read takes 16 B of one row per lane, lanes
-  // on consecutive rows, so K rows are 16 B apart modulo 128 (8 lanes then
-  // cover the 32 banks once); a transposing V read takes 8 B from each of
-  // 4 rows x 4 lanes, 32 contiguous bytes per row, so V rows are 32 B apart
-  // modulo 128.  (One stride of 64 B padding for both: the K reads 4-way
-  // and the V reads 2-way bank conflicts, conflict cycles 44% of the LDS
-  // active cycles in the counters.)
-  static constexpr int RSK = D * 2 + 16;
+  // LDS row strides (bytes), chosen by the bank-conflict counter: a K
+  // operand read takes 16 B of one row per lane (lanes on consecutive rows),
+  // a transposing V read 8 B from each of 4 rows x 4 lanes (32 contiguous
+  // bytes per row).  With rows 32 B apart modulo 128, neither conflicts:
+  // what the counter still reports comes from the staging writes.  (K rows
+  // 16 B apart, 48, 64 or 80: the K reads conflicted, a third of the LDS
+  // active cycles; one stride of 64 B padding for both: 44%.)
+  static constexpr int RSK = D * 2 + 32;
   static constexpr int RSV = D * 2 + 32;
   static constexpr int EB = KV == KV_FP8 ? 1 : 2;      // stored bytes per element
   static constexpr int ROWB = D * EB;                  // bytes of a token row (one head) in the pool
